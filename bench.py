@@ -1,0 +1,251 @@
+#!/usr/bin/env python3
+"""Decode throughput of grouped-query decode attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one gqa_decode call: one new token for each of the B sequences of
+the workload, attending over its seeded synthetic KV cache (inputs resident in
+HBM before the timed region).  Prints ONE JSON line with tokens/s, the
+roofline of the decode kernel (algorithmic bytes / average kernel time from
+HIP events on the launch stream, against 8 TB/s), and the CPU oracle timed on
+a bounded sample of the same workload.
+
+Other modes (used to produce the files under profiles/):
+    --calibrate-copy           plain device copy of a known size, for scaling
+                               the FETCH_SIZE / WRITE_SIZE counters
+    --summarize-rocprof DIR    print a summary of rocprofv3 CSV output
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, published
+METRIC = "decode tokens/sec + achieved HBM GB/s (% of peak) for GQA decode at 1 GPU"
+KERNEL_SOURCES = ["gqa_device.h", "gqa_decode_mfma.hip", "gqa_decode_valu.hip"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "grouped_query_kv_decode_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def alg_bytes(w, seq_lens) -> int:
+    """K+V bytes of the attended positions plus q and out (element bytes e)."""
+    e = 4 if w.dtype == "f32" else 2
+    n = int(seq_lens.to("cpu").clamp(0, w.Lmax).sum())
+    return 2 * w.G * n * w.d * e + 2 * w.B * w.H * w.d * e
+
+
+def load_traffic(workload_name: str):
+    """HBM traffic per dispatch from committed counter runs, if they were taken
+    on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload_name)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_hash") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_dispatch")
+
+
+def cpu_baseline(w, q, k, v, lens, out_gpu, budget_s: float):
+    """Times the oracle on the host cores over whole batches of the workload."""
+    import numpy as np
+    import torch
+    sys.path.insert(0, ROOT)
+    import oracle
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    # host copies of the attended part of the cache, one sequence at a time
+    t_copy = time.perf_counter()
+    seqs = []
+    for b in range(w.B):
+        n = max(1, min(int(lens[b]), w.Lmax))
+        seqs.append((q[b:b + 1].cpu(), k[b:b + 1, :, :n].cpu().contiguous(), v[b:b + 1, :, :n].cpu().contiguous(),
+                     lens[b:b + 1].cpu()))
+    t_copy = time.perf_counter() - t_copy
+    ora = oracle.get()
+    reps, elapsed, ref = 0, 0.0, None
+    while True:
+        t0 = time.perf_counter()
+        outs = [ora.decode(qq, kk, vv, ll, w.scale, nthreads=threads)[0] for qq, kk, vv, ll in seqs]
+        elapsed += time.perf_counter() - t0
+        reps += 1
+        if ref is None:
+            ref = np.stack(outs)
+        if elapsed >= budget_s or reps >= 20:
+            break
+    got = out_gpu.float().cpu().double().numpy()
+    err = float(np.max(np.abs(got - ref)))
+    tol = 1e-5 if w.dtype == "f32" else 2e-2
+    base = {
+        "value": w.B * reps / elapsed, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+        "sample": "%d full batch(es) of the workload (%d sequences each), binary64 C oracle, %d threads over "
+                  "(sequence, head); host copy %.2f s excluded" % (reps, w.B, threads, t_copy),
+        "seconds_per_batch": elapsed / reps,
+    }
+    parity = {"max_abs_err": err, "tol": tol, "pass": bool(err <= tol and np.isfinite(got).all())}
+    return base, parity
+
+
+def run_bench(args):
+    import torch
+    import grouped_query_kv_decode_amd as gqa
+    from grouped_query_kv_decode_amd import workloads as wl
+
+    w = wl.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    gqa.load_library()
+    kv_bytes = 2 * w.B * w.G * w.Lmax * w.d * (4 if w.dtype == "f32" else 2)
+    rot = args.rotate if args.rotate else max(1, math.ceil((1 << 30) / kv_bytes))
+    sets, decs = [], []
+    for i in range(rot):
+        q, k, v, lens = wl.make_inputs(w, dev, pad="none", seed_offset=i)
+        dec = gqa.Decoder(q, k, v, lens, w.scale)
+        sets.append((q, k, v, lens))
+        decs.append(dec)
+    torch.cuda.synchronize()
+    kind = gqa.decode_kernel_kind(w.B, w.H, w.G, w.d, w.Lmax, gqa.GQA_F32 if w.dtype == "f32" else gqa.GQA_BF16)
+
+    for i in range(args.warmup):
+        decs[i % rot]()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record(stream)
+        decs[i % rot]()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = sorted(a.elapsed_time(b) for a, b in ev)
+    avg_kernel_ms = sum(kernel_ms) / K
+    ab = alg_bytes(w, sets[0][3])  # every rotation set has the same lengths
+    achieved = ab / (avg_kernel_ms * 1e-3) / 1e9
+    ms_per_step = wall * 1e3 / K
+    traffic = load_traffic(w.name)
+
+    line = {
+        "metric": METRIC,
+        "value": w.B * K / wall,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded Gaussian caches)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "G": w.G, "d": w.d, "Lmax": w.Lmax,
+                   "ragged": w.ragged, "rotation_sets": rot,
+                   "kernel": ["valu", "mfma"][kind], "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic},
+        "alg_bytes_per_step": ab,
+        "kernel_us_avg": avg_kernel_ms * 1e3,
+        "kernel_us_median": kernel_ms[K // 2] * 1e3,
+        "hbm_gbps_wall": ab / (ms_per_step * 1e-3) / 1e9,
+    }
+    if not args.no_cpu_baseline:
+        q, k, v, lens = sets[0]
+        out = decs[0]().clone()
+        torch.cuda.synchronize()
+        base, parity = cpu_baseline(w, q, k, v, lens.cpu(), out, args.cpu_budget)
+        line["cpu_baseline"] = base
+        line["parity"] = parity
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+def calibrate_copy(args):
+    """A plain device-to-device copy of a known size (for counter scaling)."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "calls": args.steps}), flush=True)
+
+
+def _read_csvs(d, suffix):
+    rows = []
+    for f in sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True)):
+        with open(f) as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def summarize_rocprof(d):
+    """Per-kernel duration stats and per-dispatch counter means from rocprofv3 CSVs."""
+    stats = _read_csvs(d, "kernel_stats.csv")
+    out = []
+    if stats:
+        out.append("kernel stats (rocprofv3 --kernel-trace --stats):")
+        out.append("%-90s %7s %12s %12s %12s" % ("kernel", "calls", "avg_us", "min_us", "max_us"))
+        for r in stats:
+            out.append("%-90s %7s %12.2f %12.2f %12.2f" % (r["Name"][:90], r["Calls"], float(r["AverageNs"]) / 1e3,
+                                                          float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3))
+    ctr = _read_csvs(d, "counter_collection.csv")
+    if ctr:
+        agg = {}
+        for r in ctr:
+            key = (r.get("Kernel_Name", "?"), r.get("Counter_Name", "?"))
+            agg.setdefault(key, []).append(float(r.get("Counter_Value", "nan")))
+        out.append("counters (rocprofv3 --pmc), mean per dispatch:")
+        for (kname, cname), vals in sorted(agg.items()):
+            out.append("%-90s %-12s n=%-5d mean=%.1f" % (kname[:90], cname, len(vals), sum(vals) / len(vals)))
+    return "\n".join(out)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="mistral7b_bf16_B16_H32_G8_d128_L4096")
+    ap.add_argument("--rotate", type=int, default=0, help="input sets cycled through (default: >= 1 GiB of caches)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time to aim for")
+    ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--summarize-rocprof", metavar="DIR")
+    args = ap.parse_args()
+    if args.summarize_rocprof:
+        print(summarize_rocprof(args.summarize_rocprof))
+        return 0
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (collectives and sharding are out of "
+              "scope); run with --gpus 1", file=sys.stderr)
+        return 2
+    if args.calibrate_copy:
+        calibrate_copy(args)
+        return 0
+    run_bench(args)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,210 @@
+"""Grouped-query decode attention for AMD Instinct MI355X (gfx950).
+
+Thin ctypes binding over ``libgqa.so`` (C ABI in ``include/gqa.h``): argument
+marshalling only.  Every step of the computation runs in the HIP kernels; if
+the library is missing or cannot be loaded the calls raise - there is no
+fallback path.  PyTorch supplies device memory and the stream.
+
+Entry points (same names as the C ABI, without the ``gqa_`` prefix):
+    decode(q, k_cache, v_cache, seq_lens, scale, out=None, workspace=None)
+    decode_workspace_size(B, H, G, d, Lmax, dtype)
+    workspace_init(workspace)
+    meanpool_kv(w, H, G, out=None)
+    decode_kernel_kind(B, H, G, d, Lmax, dtype)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "GQAError", "decode", "decode_workspace_size", "workspace_init", "meanpool_kv",
+    "decode_kernel_kind", "status_string", "library_path", "load_library", "Decoder",
+    "GQA_F32", "GQA_BF16",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libgqa.so")
+
+GQA_F32, GQA_BF16 = 0, 1
+STATUS_NAMES = {
+    0: "GQA_OK", 1: "GQA_ERR_NULL", 2: "GQA_ERR_SHAPE", 3: "GQA_ERR_UNSUPPORTED", 4: "GQA_ERR_ALIGN",
+    5: "GQA_ERR_WORKSPACE", 6: "GQA_ERR_SCALE", 7: "GQA_ERR_HIP", 8: "GQA_ERR_SIZE",
+}
+EXPORTED = [
+    "gqa_decode_workspace_size", "gqa_workspace_init", "gqa_decode", "gqa_meanpool_kv",
+    "gqa_status_string", "gqa_last_hip_error", "gqa_decode_kernel_kind",
+]
+
+_lib = None
+
+
+class GQAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = "%s failed: %s (%s)" % (where, STATUS_NAMES.get(status, status), status_string(status))
+        if status == 7:
+            msg += ": " + load_library().gqa_last_hip_error().decode()
+        super().__init__(msg)
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library(path: str | None = None):
+    """Load libgqa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or _LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError("libgqa.so not found at %s; build it with `python -m grouped_query_kv_decode_amd.build`" % p)
+    lib = ctypes.CDLL(p)
+    vp, ci, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.gqa_decode_workspace_size.restype = sz
+    lib.gqa_decode_workspace_size.argtypes = [ci, ci, ci, ci, ci, ci]
+    lib.gqa_workspace_init.restype = ci
+    lib.gqa_workspace_init.argtypes = [vp, sz, vp]
+    lib.gqa_decode.restype = ci
+    lib.gqa_decode.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, ci, ctypes.c_float, ci, vp, vp, sz, vp]
+    lib.gqa_meanpool_kv.restype = ci
+    lib.gqa_meanpool_kv.argtypes = [vp, ci, ci, ci, ci, vp, vp]
+    lib.gqa_status_string.restype = ctypes.c_char_p
+    lib.gqa_status_string.argtypes = [ci]
+    lib.gqa_last_hip_error.restype = ctypes.c_char_p
+    lib.gqa_last_hip_error.argtypes = []
+    lib.gqa_decode_kernel_kind.restype = ci
+    lib.gqa_decode_kernel_kind.argtypes = [ci, ci, ci, ci, ci, ci]
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().gqa_status_string(int(status)).decode()
+
+
+def _dtype_code(dt) -> int:
+    import torch
+    if dt == torch.float32:
+        return GQA_F32
+    if dt == torch.bfloat16:
+        return GQA_BF16
+    raise TypeError("unsupported dtype %s (float32 or bfloat16)" % dt)
+
+
+def _stream_handle(device) -> int:
+    import torch
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def decode_workspace_size(B, H, G, d, Lmax, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
+    return int(load_library().gqa_decode_workspace_size(B, H, G, d, Lmax, code))
+
+
+def decode_kernel_kind(B, H, G, d, Lmax, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
+    return int(load_library().gqa_decode_kernel_kind(B, H, G, d, Lmax, code))
+
+
+def workspace_init(workspace) -> None:
+    st = load_library().gqa_workspace_init(workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                           _stream_handle(workspace.device))
+    if st:
+        raise GQAError(st, "gqa_workspace_init")
+
+
+# One cleared workspace per (device, stream), grown on demand.
+_ws_cache: dict = {}
+
+
+def _workspace_for(nbytes: int, device):
+    import torch
+    key = (device.index, _stream_handle(device))
+    ws = _ws_cache.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _ws_cache[key] = ws
+    return ws
+
+
+def _prepare(q, k_cache, v_cache, seq_lens, scale, out, workspace):
+    """Checks the tensors and returns (ctypes argument tuple without the stream, out, workspace)."""
+    import torch
+    B, H, d = q.shape
+    Bk, G, Lmax, dk = k_cache.shape
+    if Bk != B or dk != d or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("shape mismatch: q %s, k %s, v %s" % (tuple(q.shape), tuple(k_cache.shape), tuple(v_cache.shape)))
+    if not (q.dtype == k_cache.dtype == v_cache.dtype):
+        raise TypeError("q, k_cache and v_cache must share one dtype")
+    if seq_lens.dtype != torch.int32 or tuple(seq_lens.shape) != (B,):
+        raise TypeError("seq_lens must be int32 of shape [B]")
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("seq_lens", seq_lens)):
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+        if t.device != q.device or t.device.type != "cuda":
+            raise ValueError("%s must be on the GPU of q" % name)
+    code = _dtype_code(q.dtype)
+    if out is None:
+        out = torch.empty((B, H, d), dtype=q.dtype, device=q.device)
+    elif tuple(out.shape) != (B, H, d) or out.dtype != q.dtype or not out.is_contiguous() or out.device != q.device:
+        raise ValueError("out must be a contiguous [B,H,d] tensor of q's dtype on q's GPU")
+    need = decode_workspace_size(B, H, G, d, Lmax, code)
+    if workspace is None and need > 0:
+        workspace = _workspace_for(need, q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    args = (q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr(), B, H, G, d, Lmax,
+            float(scale), code, out.data_ptr(), ws_ptr, ws_bytes)
+    return args, out, workspace
+
+
+def decode(q, k_cache, v_cache, seq_lens, scale: float, out=None, workspace=None):
+    """out[B,H,d] = grouped-query decode attention (see include/gqa.h).
+
+    q [B,H,d], k_cache/v_cache [B,G,Lmax,d] (float32 or bfloat16, one dtype,
+    contiguous, on one GPU), seq_lens [B] int32 on the same GPU.  Enqueued on
+    torch's current stream.
+    """
+    args, out, _ = _prepare(q, k_cache, v_cache, seq_lens, scale, out, workspace)
+    st = load_library().gqa_decode(*args, _stream_handle(q.device))
+    if st:
+        raise GQAError(st, "gqa_decode")
+    return out
+
+
+class Decoder:
+    """A decode call bound to fixed tensors and to the stream current at
+    construction; each call() is one C-ABI call with pre-marshalled
+    arguments (for tight loops: serving steps, benchmarks)."""
+
+    def __init__(self, q, k_cache, v_cache, seq_lens, scale: float, out=None, workspace=None):
+        self._keep = (q, k_cache, v_cache, seq_lens)
+        self._args, self.out, self.workspace = _prepare(q, k_cache, v_cache, seq_lens, scale, out, workspace)
+        self._args = self._args + (_stream_handle(q.device),)
+        self._fn = load_library().gqa_decode
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st:
+            raise GQAError(st, "gqa_decode")
+        return self.out
+
+
+def meanpool_kv(w, H: int, G: int, out=None):
+    """w_out[d_model, G*h] = per-group mean of the head column blocks of w[d_model, H*h] (float32)."""
+    import torch
+    if w.dtype != torch.float32 or w.dim() != 2 or not w.is_contiguous() or w.device.type != "cuda":
+        raise ValueError("w must be a contiguous float32 [d_model, H*h] tensor on the GPU")
+    d_model, cols = w.shape
+    if H < 1 or cols % H:
+        raise ValueError("w has %d columns, not a multiple of H=%d" % (cols, H))
+    h = cols // H
+    if out is None:
+        out = torch.empty((d_model, G * h), dtype=torch.float32, device=w.device)
+    st = load_library().gqa_meanpool_kv(w.data_ptr(), d_model, H, G, h, out.data_ptr(), _stream_handle(w.device))
+    if st:
+        raise GQAError(st, "gqa_meanpool_kv")
+    return out

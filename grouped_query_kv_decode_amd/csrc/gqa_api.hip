@@ -1,0 +1,201 @@
+// Host side of libgqa.so: argument checks, launch planning and the C ABI
+// declared in include/gqa.h.  No allocation, no synchronisation.
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <string>
+
+#include "gqa.h"
+#include "gqa_device.h"
+
+namespace {
+
+thread_local std::string g_last_hip_error;
+
+gqa_status hip_fail(hipError_t e) {
+  g_last_hip_error = hipGetErrorString(e);
+  return GQA_ERR_HIP;
+}
+
+int env_int(const char *name, int dflt) {
+  const char *v = getenv(name);
+  if (!v || !*v) return dflt;
+  char *end = nullptr;
+  const long x = strtol(v, &end, 10);
+  return (end && *end == 0 && x > 0 && x < (1L << 30)) ? (int)x : dflt;
+}
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
+int next_pow2(int x) {
+  int p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+
+enum { KIND_VALU = 0, KIND_MFMA = 1 };
+
+struct Plan {
+  int kind;
+  int chunk, S, HC, RC, HB;
+  unsigned grid;
+  size_t cnt_off, ml_off, o_off, ws_bytes;
+};
+
+gqa_status check_shape(int B, int H, int G, int d, int Lmax, gqa_dtype dt) {
+  if (dt != GQA_F32 && dt != GQA_BF16) return GQA_ERR_UNSUPPORTED;
+  if (B < 0 || H < 1 || G < 1 || d < 1 || Lmax < 1 || H % G != 0) return GQA_ERR_SHAPE;
+  if (d != 64 && d != 128) return GQA_ERR_UNSUPPORTED;
+  return GQA_OK;
+}
+
+// Decode launch plan.  One workgroup per (b, g, head chunk, split); splits
+// are sized so that the grid holds about GQA_TARGET_WGS workgroups (default
+// 2048, eight per compute unit) with at most GQA_MAX_CHUNK positions each.
+gqa_status make_plan(int B, int H, int G, int d, int Lmax, gqa_dtype dt, Plan *pl) {
+  const int r = H / G;
+  const char *force = getenv("GQA_KERNEL");
+  int kind = dt == GQA_BF16 ? KIND_MFMA : KIND_VALU;
+  if (force && strcmp(force, "valu") == 0) kind = KIND_VALU;
+  if (kind == KIND_MFMA && r > 64) kind = KIND_VALU;
+  pl->kind = kind;
+  if (kind == KIND_MFMA) {
+    const int hb = (r + 15) / 16;
+    pl->HB = hb <= 1 ? 1 : (hb <= 2 ? 2 : 4);
+    pl->RC = 0;
+    pl->HC = 1;
+  } else {
+    pl->RC = next_pow2(r < 8 ? r : 8);
+    pl->HC = ceil_div(r, pl->RC);
+    pl->HB = 0;
+  }
+  const long units = (long)B * G * pl->HC;
+  const int target = env_int("GQA_TARGET_WGS", 2048);
+  const int max_chunk = env_int("GQA_MAX_CHUNK", 2048);
+  int chunk = env_int("GQA_CHUNK", 0);
+  if (chunk == 0) {
+    long S = (target + units - 1) / units;
+    if (S < 1) S = 1;
+    chunk = (int)round_up((size_t)ceil_div(Lmax, S), 128);
+    if (chunk > max_chunk) chunk = (int)round_up((size_t)max_chunk, 128);
+  }
+  if (chunk > Lmax) chunk = Lmax;
+  pl->chunk = chunk;
+  pl->S = ceil_div(Lmax, chunk);
+  const unsigned long long grid = (unsigned long long)units * pl->S;
+  if (grid == 0 || grid > 0x7fffffffULL) return GQA_ERR_SIZE;
+  pl->grid = (unsigned)grid;
+  if (pl->S > 1) {
+    pl->cnt_off = 0;
+    pl->ml_off = round_up((size_t)units * sizeof(unsigned), 256);
+    pl->o_off = pl->ml_off + round_up((size_t)B * H * pl->S * sizeof(float2), 256);
+    pl->ws_bytes = pl->o_off + (size_t)B * H * pl->S * d * sizeof(float);
+  } else {
+    pl->cnt_off = pl->ml_off = pl->o_off = pl->ws_bytes = 0;
+  }
+  return GQA_OK;
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+size_t gqa_decode_workspace_size(int B, int H, int G, int d, int Lmax, gqa_dtype dtype) {
+  if (check_shape(B, H, G, d, Lmax, dtype) != GQA_OK || B == 0) return 0;
+  Plan pl;
+  if (make_plan(B, H, G, d, Lmax, dtype, &pl) != GQA_OK) return 0;
+  return pl.ws_bytes;
+}
+
+int gqa_decode_kernel_kind(int B, int H, int G, int d, int Lmax, gqa_dtype dtype) {
+  if (check_shape(B, H, G, d, Lmax, dtype) != GQA_OK) return -1;
+  Plan pl;
+  if (make_plan(B > 0 ? B : 1, H, G, d, Lmax, dtype, &pl) != GQA_OK) return -1;
+  return pl.kind;
+}
+
+gqa_status gqa_workspace_init(void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (workspace_bytes == 0) return GQA_OK;
+  if (!workspace) return GQA_ERR_NULL;
+  const hipError_t e = gqa::launch_fill_zero(workspace, workspace_bytes, stream);
+  return e == hipSuccess ? GQA_OK : hip_fail(e);
+}
+
+gqa_status gqa_decode(const void *q, const void *k_cache, const void *v_cache, const int32_t *seq_lens, int B, int H,
+                      int G, int d, int Lmax, float scale, gqa_dtype dtype, void *out, void *workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+  gqa_status st = check_shape(B, H, G, d, Lmax, dtype);
+  if (st != GQA_OK) return st;
+  if (B == 0) return GQA_OK;
+  if (!q || !k_cache || !v_cache || !seq_lens || !out) return GQA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) || !aligned(seq_lens, 4))
+    return GQA_ERR_ALIGN;
+  const double sl2 = (double)scale * 1.4426950408889634;
+  if (!isfinite(scale) || !isfinite((float)sl2)) return GQA_ERR_SCALE;
+  Plan pl;
+  st = make_plan(B, H, G, d, Lmax, dtype, &pl);
+  if (st != GQA_OK) return st;
+  if (pl.ws_bytes > 0) {
+    if (!workspace) return GQA_ERR_NULL;
+    if (workspace_bytes < pl.ws_bytes) return GQA_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return GQA_ERR_ALIGN;
+  }
+
+  gqa::DecodeParams p;
+  p.q = q;
+  p.k = k_cache;
+  p.v = v_cache;
+  p.seq_lens = seq_lens;
+  p.out = out;
+  char *ws = static_cast<char *>(workspace);
+  p.ws_cnt = pl.ws_bytes ? reinterpret_cast<unsigned *>(ws + pl.cnt_off) : nullptr;
+  p.ws_ml = pl.ws_bytes ? reinterpret_cast<float2 *>(ws + pl.ml_off) : nullptr;
+  p.ws_o = pl.ws_bytes ? reinterpret_cast<float *>(ws + pl.o_off) : nullptr;
+  p.B = B;
+  p.H = H;
+  p.G = G;
+  p.Lmax = Lmax;
+  p.r = H / G;
+  p.S = pl.S;
+  p.chunk = pl.chunk;
+  p.HC = pl.HC;
+  p.scale_log2 = (float)sl2;
+
+  const hipError_t e = pl.kind == KIND_MFMA ? gqa::launch_decode_mfma(p, d, pl.HB, pl.grid, stream)
+                                            : gqa::launch_decode_valu(p, (int)dtype, d, pl.RC, pl.grid, stream);
+  return e == hipSuccess ? GQA_OK : hip_fail(e);
+}
+
+gqa_status gqa_meanpool_kv(const float *w, int d_model, int H, int G, int h, float *w_out, hipStream_t stream) {
+  if (d_model < 0 || H < 1 || G < 1 || H % G != 0) return GQA_ERR_SHAPE;
+  if (h < 1) return GQA_ERR_UNSUPPORTED;
+  if (d_model == 0) return GQA_OK;
+  if (!w || !w_out) return GQA_ERR_NULL;
+  if (!aligned(w, 4) || !aligned(w_out, 4)) return GQA_ERR_ALIGN;
+  const unsigned long long total = (unsigned long long)d_model * G * h;
+  if ((unsigned long long)d_model * H * h > (1ULL << 40) || (total + 255) / 256 > 0x7fffffffULL) return GQA_ERR_SIZE;
+  const hipError_t e = gqa::launch_meanpool(w, d_model, H, G, h, w_out, stream);
+  return e == hipSuccess ? GQA_OK : hip_fail(e);
+}
+
+const char *gqa_status_string(gqa_status s) {
+  switch (s) {
+    case GQA_OK: return "ok";
+    case GQA_ERR_NULL: return "a required pointer is NULL";
+    case GQA_ERR_SHAPE: return "invalid shape (sizes must be positive and H divisible by G)";
+    case GQA_ERR_UNSUPPORTED: return "unsupported head dimension or dtype";
+    case GQA_ERR_ALIGN: return "pointer not aligned (16 bytes for tensors, 256 for the workspace)";
+    case GQA_ERR_WORKSPACE: return "workspace smaller than gqa_decode_workspace_size()";
+    case GQA_ERR_SCALE: return "scale is not finite";
+    case GQA_ERR_HIP: return "HIP runtime error";
+    case GQA_ERR_SIZE: return "problem size exceeds the supported index range";
+  }
+  return "unknown status";
+}
+
+const char *gqa_last_hip_error(void) { return g_last_hip_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,279 @@
+// Grouped-query decode attention on the matrix cores (bfloat16, gfx950).
+//
+// One workgroup (4 waves) owns (sequence b, K/V head g, split s) and streams
+// that K/V head's positions of the split from HBM once, serving all r = H/G
+// query heads of the group from each tile (wikillm "Grouped-query attention
+// (GQA)", Overview; the decode-step block of its Implementation sketch gives
+// the per-head softmax(scale * q.K) . V that is computed here).
+//
+// Each wave takes 32-position tiles.  With v_mfma_f32_16x16x32_bf16
+// (A: 16x32, B: 32x16, both 8 bf16 per lane; lane l holds row / column l%16):
+//   scores^T[16 pos x 16 heads] = K_tile[16 x D] . Q^T[D x 16]
+//     A = K rows straight from global memory (16 bytes per lane), B = q.
+//     Row m of half h is position 8*(m/4) + 4*h + m%4 of the tile, so lane
+//     group c = l/16 ends up holding the scores of positions 8c .. 8c+7.
+//   out^T[16 dims x 16 heads] += V_tile^T[16 x 32 pos] . P^T[32 pos x 16]
+//     B = the probabilities already in the lane (no data movement); A needs
+//     8 positions of one dimension per lane.  Lane (c, n) loads rows 8c+u,
+//     dims 8n .. 8n+7 (D = 128) with coalesced 16-byte loads and transposes
+//     the 8x8 block in registers; MFMA number db then covers dimensions
+//     8m + db, m = 0..15, so the output lands as 32 contiguous dims per lane.
+// Heads beyond r in a 16-head block are zero queries whose results are
+// discarded.  The reduction index order inside an MFMA is free, which is
+// why the position and dimension permutations above need no other fix-up.
+#include <type_traits>
+
+#include "gqa_device.h"
+
+namespace gqa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                 0, 0);
+}
+
+// max / sum over the four lanes l, l^16, l^32, l^48 (one head's lane groups)
+__device__ __forceinline__ float group_max(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float group_sum(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Element e (0..7) of eight 16-bit rows, packed as one MFMA operand:
+// dword k = (row 2k element e, row 2k+1 element e).
+template <int E, typename Row>
+__device__ __forceinline__ u32x4 column(const Row *rows) {
+  constexpr unsigned sel = (E & 1) ? 0x07060302u : 0x05040100u;
+  u32x4 a;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) a[k] = __builtin_amdgcn_perm(rows[2 * k + 1][E >> 1], rows[2 * k][E >> 1], sel);
+  return a;
+}
+
+// out^T += V^T . P^T for dimension blocks DBI .. DB-1.
+template <int DBI, int DB, int HB, typename Row>
+__device__ __forceinline__ void pv_steps(f32x4 (&o)[HB][DB], const Row *vR, const u32x4 *pB) {
+  if constexpr (DBI < DB) {
+    const u32x4 a = column<DBI>(vR);
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) o[hb][DBI] = mfma(a, pB[hb], o[hb][DBI]);
+    pv_steps<DBI + 1, DB, HB>(o, vR, pB);
+  }
+}
+
+template <int D, int HB>
+__global__ __launch_bounds__(256) void decode_mfma(DecodeParams p) {
+  static_assert(D == 64 || D == 128, "head dim");
+  constexpr int KB = D / 32;  // QK MFMAs per 16-position half
+  constexpr int DB = D / 16;  // PV MFMAs (dimension blocks)
+  typedef typename std::conditional<D == 128, u32x4, u32x2>::type VRow;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = lane >> 4, nn = lane & 15;
+
+  unsigned id = blockIdx.x;
+  const int s = id % p.S;
+  id /= p.S;
+  const int g = id % p.G;
+  const int b = id / p.G;
+
+  const int n = clamp_len(p, b);
+  const int nsplit = num_splits(n, p.chunk);
+  if (s >= nsplit) return;
+  const int head0 = g * p.r;
+  if (n == 0) {
+    write_zero_heads<__bf16, D>(p, b, head0, p.r);
+    return;
+  }
+  const int t0 = s * p.chunk, t1 = min(t0 + p.chunk, n);
+
+  // B operand of the score MFMAs: q of head hb*16 + nn, dims kb*32 + 8c .. +7.
+  u32x4 qB[HB][KB];
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) {
+    const int j = hb * 16 + nn;
+    const __bf16 *qp = static_cast<const __bf16 *>(p.q) + ((size_t)b * p.H + head0 + j) * D + 8 * c;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+      qB[hb][kb] = j < p.r ? *reinterpret_cast<const u32x4 *>(qp + kb * 32) : u32x4{0u, 0u, 0u, 0u};
+  }
+
+  const size_t slab = ((size_t)b * p.G + g) * (size_t)p.Lmax * D;
+  const __bf16 *kp = static_cast<const __bf16 *>(p.k) + slab + 8 * c;
+  const __bf16 *vp = static_cast<const __bf16 *>(p.v) + slab + (D == 128 ? 8 : 4) * nn;
+
+  f32x4 o[HB][DB];
+  float m[HB], l[HB];
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) {
+    m[hb] = kNegInf;
+    l[hb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[hb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  for (int tt = t0 + 32 * wave; tt < t1; tt += 128) {
+    // K rows for the two score halves, V rows 8c .. 8c+7 of the tile.
+    u32x4 kA[2][KB];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int t = tt + 8 * (nn >> 2) + 4 * h + (nn & 3);
+      const size_t row = (size_t)min(t, t1 - 1);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) kA[h][kb] = *reinterpret_cast<const u32x4 *>(kp + row * D + kb * 32);
+    }
+    VRow vR[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const size_t row = (size_t)min(tt + 8 * c + u, t1 - 1);
+      vR[u] = *reinterpret_cast<const VRow *>(vp + row * D);
+    }
+
+    u32x4 pB[HB];
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+      f32x4 acc[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) acc[h] = mfma(kA[h][kb], qB[hb][kb], acc[h]);
+      }
+      // lane (c, nn): scores of positions tt + 8c + u, u = 4h + i, head nn
+      float sc[8];
+      float mt = kNegInf;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float x = acc[u >> 2][u & 3] * p.scale_log2;
+        sc[u] = tt + 8 * c + u < t1 ? x : kNegInf;
+        mt = fmaxf(mt, sc[u]);
+      }
+      mt = group_max(mt);
+      const float mn = fmaxf(m[hb], mt);
+      const float sh = safe_shift(mn);
+      const float alpha = fast_exp2(m[hb] - sh);
+      m[hb] = mn;
+      float pv[8], sum = 0.f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        pv[u] = fast_exp2(sc[u] - sh);
+        sum += pv[u];
+      }
+      l[hb] = l[hb] * alpha + sum;
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[hb][db] *= alpha;
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const bf16x2 t2 = {(__bf16)pv[2 * k], (__bf16)pv[2 * k + 1]};  // round to nearest even
+        pB[hb][k] = __builtin_bit_cast(unsigned, t2);
+      }
+    }
+
+    pv_steps<0, DB, HB>(o, vR, pB);
+  }
+
+  // Per-head weight sums: add the four lane groups.
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) l[hb] = group_sum(l[hb]);
+
+  // Merge the four waves through LDS, in wave order (deterministic).
+  constexpr int NHB = 16 * HB;
+  constexpr int LD = D + 4;
+  __shared__ float sm_m[4][NHB], sm_l[4][NHB];
+  __shared__ float sm_o[NHB * LD];
+  if (c == 0) {
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+      sm_m[wave][hb * 16 + nn] = m[hb];
+      sm_l[wave][hb * 16 + nn] = l[hb];
+    }
+  }
+  __syncthreads();
+  float a_self[HB];
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) {
+    const int j = hb * 16 + nn;
+    const float M = fmaxf(fmaxf(sm_m[0][j], sm_m[1][j]), fmaxf(sm_m[2][j], sm_m[3][j]));
+    a_self[hb] = fast_exp2(m[hb] - safe_shift(M));
+  }
+  for (int w = 0; w < 4; ++w) {
+    if (wave == w) {
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) {
+        float *row = sm_o + (hb * 16 + nn) * LD;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            // output row m = 4c + i of MFMA db holds dimension dpm*m + db
+            const int dim = (D == 128 ? 8 : 4) * (4 * c + i) + db;
+            const float add = o[hb][db][i] * a_self[hb];
+            row[dim] = w == 0 ? add : row[dim] + add;
+          }
+      }
+    }
+    __syncthreads();
+  }
+
+  for (int idx = threadIdx.x; idx < p.r * (D / 4); idx += blockDim.x) {
+    const int j = idx / (D / 4), cc = (idx % (D / 4)) * 4;
+    const float M = fmaxf(fmaxf(sm_m[0][j], sm_m[1][j]), fmaxf(sm_m[2][j], sm_m[3][j]));
+    const float shj = safe_shift(M);
+    float L = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) L += sm_l[w][j] * fast_exp2(sm_m[w][j] - shj);
+    const float *row = sm_o + j * LD + cc;
+    if (nsplit == 1) {
+      const float inv = 1.f / L;
+      Store<__bf16>::four(p.out, ((size_t)b * p.H + head0 + j) * D + cc, row[0] * inv, row[1] * inv, row[2] * inv,
+                          row[3] * inv);
+    } else {
+      const size_t hs = ((size_t)b * p.H + head0 + j) * p.S + s;
+      *reinterpret_cast<float4 *>(p.ws_o + hs * D + cc) = make_float4(row[0], row[1], row[2], row[3]);
+      if (cc == 0) p.ws_ml[hs] = make_float2(M, L);
+    }
+  }
+  if (nsplit == 1) return;
+  if (!arrive_last(p.ws_cnt + (size_t)b * p.G + g, nsplit)) return;
+  merge_splits<__bf16, D>(p, b, head0, p.r, nsplit);
+}
+
+template <int D, int HB>
+hipError_t launch_t(const DecodeParams &p, unsigned grid, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_mfma<D, HB>), dim3(grid), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_hb(const DecodeParams &p, int HB, unsigned grid, hipStream_t stream) {
+  switch (HB) {
+    case 1: return launch_t<D, 1>(p, grid, stream);
+    case 2: return launch_t<D, 2>(p, grid, stream);
+    case 4: return launch_t<D, 4>(p, grid, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode_mfma(const DecodeParams &p, int D, int HB, unsigned grid, hipStream_t stream) {
+  return D == 64 ? launch_hb<64>(p, HB, grid, stream) : launch_hb<128>(p, HB, grid, stream);
+}
+
+}  // namespace gqa

@@ -1,0 +1,263 @@
+// Grouped-query decode attention on the vector ALUs (binary32 and bfloat16).
+//
+// One workgroup (4 waves) owns (sequence b, K/V head g, head chunk hc, split
+// s): it streams positions [s*chunk, min((s+1)*chunk, len_b)) of K/V head g
+// once and serves up to RC query heads of the group from every row it loads
+// (wikillm "Grouped-query attention (GQA)", Overview: every query head of a
+// group attends with the group's single key and value head).
+//
+// Lane layout: a cache row of D elements is spread over LPR lanes, 16 bytes
+// per lane, so one wave-wide 128-bit load covers RPW consecutive rows.  Each
+// row group keeps its own online softmax state; states are merged across row
+// groups with cross-lane shuffles and across waves through LDS.
+#include "gqa_device.h"
+
+namespace gqa {
+namespace {
+
+template <typename T> struct Elems;
+template <> struct Elems<float> {
+  static constexpr int kPerLane = 4;
+  __device__ static void widen(const uint4 &u, float *f) {
+    f[0] = __uint_as_float(u.x);
+    f[1] = __uint_as_float(u.y);
+    f[2] = __uint_as_float(u.z);
+    f[3] = __uint_as_float(u.w);
+  }
+};
+template <> struct Elems<__bf16> {
+  static constexpr int kPerLane = 8;
+  // bfloat16 -> binary32 is exact: the bf16 bits become the upper half.
+  __device__ static void widen(const uint4 &u, float *f) {
+    const unsigned w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+};
+
+// Sum over aligned groups of LPR lanes; every lane of the group gets the sum.
+template <int LPR>
+__device__ __forceinline__ float row_sum(float x) {
+  // xor 1 and xor 2 inside each quad, then the half-row and row mirrors
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
+  if (LPR >= 8) x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));
+  if (LPR >= 16) x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));
+  if (LPR >= 32) x += __shfl_xor(x, 16);
+  return x;
+}
+
+template <typename T, int D, int RC, int U>
+__global__ __launch_bounds__(256) void decode_valu(DecodeParams p) {
+  constexpr int EPL = Elems<T>::kPerLane;  // elements per lane per row
+  constexpr int LPR = D / EPL;             // lanes per row
+  constexpr int RPW = 64 / LPR;            // rows per wave per load
+  constexpr int NRG = 4 * RPW;             // row groups per workgroup
+  static_assert(LPR >= 4 && LPR <= 32, "row must span 4..32 lanes");
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane % LPR;
+  const int rg = wave * RPW + lane / LPR;
+
+  unsigned id = blockIdx.x;
+  const int s = id % p.S;
+  id /= p.S;
+  const int hc = id % p.HC;
+  id /= p.HC;
+  const int g = id % p.G;
+  const int b = id / p.G;
+
+  const int n = clamp_len(p, b);
+  const int nsplit = num_splits(n, p.chunk);
+  if (s >= nsplit) return;
+  const int jbase = hc * RC;
+  const int nh = min(RC, p.r - jbase);
+  const int head0 = g * p.r + jbase;
+  if (n == 0) {
+    write_zero_heads<T, D>(p, b, head0, nh);
+    return;
+  }
+  const int t0 = s * p.chunk, t1 = min(t0 + p.chunk, n);
+
+  // Query rows of the served heads, pre-multiplied by scale*log2(e).
+  float qf[RC][EPL];
+#pragma unroll
+  for (int j = 0; j < RC; ++j) {
+    if (j < nh) {
+      const uint4 u = *reinterpret_cast<const uint4 *>(static_cast<const T *>(p.q) +
+                                                      ((size_t)b * p.H + head0 + j) * D + sub * EPL);
+      Elems<T>::widen(u, qf[j]);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) qf[j][e] *= p.scale_log2;
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) qf[j][e] = 0.f;
+    }
+  }
+
+  const size_t slab = ((size_t)b * p.G + g) * (size_t)p.Lmax * D;
+  const T *kp = static_cast<const T *>(p.k) + slab + sub * EPL;
+  const T *vp = static_cast<const T *>(p.v) + slab + sub * EPL;
+
+  float m[RC], l[RC], o[RC][EPL];
+#pragma unroll
+  for (int j = 0; j < RC; ++j) {
+    m[j] = kNegInf;
+    l[j] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[j][e] = 0.f;
+  }
+
+  for (int tb = t0; tb < t1; tb += NRG * U) {
+    uint4 kr[U], vr[U];
+    bool ok[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = tb + u * NRG + rg;
+      ok[u] = t < t1;
+      const size_t row = (size_t)(ok[u] ? t : t1 - 1);  // never past the length
+      kr[u] = *reinterpret_cast<const uint4 *>(kp + row * D);
+      vr[u] = *reinterpret_cast<const uint4 *>(vp + row * D);
+    }
+    float sc[U][RC];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float kf[EPL];
+      Elems<T>::widen(kr[u], kf);
+#pragma unroll
+      for (int j = 0; j < RC; ++j) {
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc = fmaf(qf[j][e], kf[e], acc);
+        acc = row_sum<LPR>(acc);
+        sc[u][j] = ok[u] ? acc : kNegInf;
+      }
+    }
+    float sh[RC];
+#pragma unroll
+    for (int j = 0; j < RC; ++j) {
+      float mt = sc[0][j];
+#pragma unroll
+      for (int u = 1; u < U; ++u) mt = fmaxf(mt, sc[u][j]);
+      const float mn = fmaxf(m[j], mt);
+      sh[j] = safe_shift(mn);
+      const float alpha = fast_exp2(m[j] - sh[j]);
+      m[j] = mn;
+      l[j] *= alpha;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[j][e] *= alpha;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float vf[EPL];
+      Elems<T>::widen(vr[u], vf);
+#pragma unroll
+      for (int j = 0; j < RC; ++j) {
+        const float pj = fast_exp2(sc[u][j] - sh[j]);
+        l[j] += pj;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[j][e] = fmaf(pj, vf[e], o[j][e]);
+      }
+    }
+  }
+
+  // Merge the row groups of this wave (lanes lane ^ LPR, ^ 2LPR, ...).
+#pragma unroll
+  for (int off = LPR; off < 64; off <<= 1) {
+#pragma unroll
+    for (int j = 0; j < RC; ++j) {
+      const float m2 = __shfl_xor(m[j], off);
+      const float l2 = __shfl_xor(l[j], off);
+      const float mn = fmaxf(m[j], m2);
+      const float shj = safe_shift(mn);
+      const float a1 = fast_exp2(m[j] - shj), a2 = fast_exp2(m2 - shj);
+      m[j] = mn;
+      l[j] = l[j] * a1 + l2 * a2;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[j][e] = o[j][e] * a1 + __shfl_xor(o[j][e], off) * a2;
+    }
+  }
+
+  // Merge the four waves through LDS, in wave order.
+  __shared__ float sm_m[4][RC], sm_l[4][RC];
+  __shared__ float sm_o[RC][D];
+  if (lane == 0) {
+#pragma unroll
+    for (int j = 0; j < RC; ++j) {
+      sm_m[wave][j] = m[j];
+      sm_l[wave][j] = l[j];
+    }
+  }
+  __syncthreads();
+  float a_self[RC];
+#pragma unroll
+  for (int j = 0; j < RC; ++j) {
+    const float M = fmaxf(fmaxf(sm_m[0][j], sm_m[1][j]), fmaxf(sm_m[2][j], sm_m[3][j]));
+    a_self[j] = fast_exp2(m[j] - safe_shift(M));
+  }
+  for (int w = 0; w < 4; ++w) {
+    if (wave == w && lane < LPR) {
+#pragma unroll
+      for (int j = 0; j < RC; ++j)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          const float add = o[j][e] * a_self[j];
+          sm_o[j][sub * EPL + e] = w == 0 ? add : sm_o[j][sub * EPL + e] + add;
+        }
+    }
+    __syncthreads();
+  }
+
+  // This workgroup's result for its heads: final output, or a split partial.
+  for (int idx = threadIdx.x; idx < nh * (D / 4); idx += blockDim.x) {
+    const int j = idx / (D / 4), c = (idx % (D / 4)) * 4;
+    const float M = fmaxf(fmaxf(sm_m[0][j], sm_m[1][j]), fmaxf(sm_m[2][j], sm_m[3][j]));
+    const float shj = safe_shift(M);
+    float L = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) L += sm_l[w][j] * fast_exp2(sm_m[w][j] - shj);
+    if (nsplit == 1) {
+      const float inv = 1.f / L;
+      Store<T>::four(p.out, ((size_t)b * p.H + head0 + j) * D + c, sm_o[j][c] * inv, sm_o[j][c + 1] * inv,
+                     sm_o[j][c + 2] * inv, sm_o[j][c + 3] * inv);
+    } else {
+      const size_t hs = ((size_t)b * p.H + head0 + j) * p.S + s;
+      *reinterpret_cast<float4 *>(p.ws_o + hs * D + c) =
+          make_float4(sm_o[j][c], sm_o[j][c + 1], sm_o[j][c + 2], sm_o[j][c + 3]);
+      if (c == 0) p.ws_ml[hs] = make_float2(M, L);
+    }
+  }
+  if (nsplit == 1) return;
+  if (!arrive_last(p.ws_cnt + ((size_t)b * p.G + g) * p.HC + hc, nsplit)) return;
+  merge_splits<T, D>(p, b, head0, nh, nsplit);
+}
+
+template <typename T, int D, int RC>
+hipError_t launch_t(const DecodeParams &p, unsigned grid, hipStream_t stream) {
+  constexpr int U = RC <= 4 ? 8 : 4;
+  hipLaunchKernelGGL((decode_valu<T, D, RC, U>), dim3(grid), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_rc(const DecodeParams &p, int RC, unsigned grid, hipStream_t stream) {
+  switch (RC) {
+    case 1: return launch_t<T, D, 1>(p, grid, stream);
+    case 2: return launch_t<T, D, 2>(p, grid, stream);
+    case 4: return launch_t<T, D, 4>(p, grid, stream);
+    case 8: return launch_t<T, D, 8>(p, grid, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode_valu(const DecodeParams &p, int dtype, int D, int RC, unsigned grid, hipStream_t stream) {
+  if (dtype == 0) return D == 64 ? launch_rc<float, 64>(p, RC, grid, stream) : launch_rc<float, 128>(p, RC, grid, stream);
+  return D == 64 ? launch_rc<__bf16, 64>(p, RC, grid, stream) : launch_rc<__bf16, 128>(p, RC, grid, stream);
+}
+
+}  // namespace gqa

@@ -1,0 +1,126 @@
+// Device-side pieces shared by the decode kernels: launch parameters, the
+// split-partial format, the arrival counter protocol and the log-sum-exp merge
+// of split partials.
+//
+// Decode semantics follow the decode-step block of the Implementation sketch
+// on the wikillm page "Grouped-query attention (GQA)": per query head, softmax
+// of the scaled scores against the keys of its group's K/V head, then the
+// probability-weighted sum of that head's value rows.  The softmax is taken
+// online over tiles and across context splits; merging (m, l, o) partials with
+// weights exp2(m_s - max_s m_s) gives the same quotient as the plain softmax.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gqa {
+
+struct DecodeParams {
+  const void *q;           // [B, H, D]
+  const void *k;           // [B, G, Lmax, D]
+  const void *v;           // [B, G, Lmax, D]
+  const int32_t *seq_lens; // [B]
+  void *out;               // [B, H, D]
+  float *ws_o;             // [B, H, S, D]  un-normalised split outputs
+  float2 *ws_ml;           // [B, H, S]     (running max in log2 units, sum of weights)
+  unsigned *ws_cnt;        // [B * G * HC]  arrival counters, zero between calls
+  int B, H, G, Lmax;
+  int r;                   // query heads per K/V head, H / G
+  int S;                   // splits per (b, g) in the grid
+  int chunk;               // positions per split
+  int HC;                  // head chunks per (b, g) in the grid (VALU kernel)
+  float scale_log2;        // scale * log2(e): scores are kept in log2 units
+};
+
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kNegInf = -__builtin_inff();
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Shift used with a running maximum: keeps exp2(x - shift) free of
+// (-inf) - (-inf) when nothing has been seen yet.
+__device__ __forceinline__ float safe_shift(float m) { return m == kNegInf ? 0.f : m; }
+
+__device__ __forceinline__ int clamp_len(const DecodeParams &p, int b) {
+  int n = p.seq_lens[b];
+  return n < 0 ? 0 : (n > p.Lmax ? p.Lmax : n);
+}
+
+__device__ __forceinline__ int num_splits(int n, int chunk) { return n > 0 ? (n + chunk - 1) / chunk : 1; }
+
+template <typename T> struct Store;
+template <> struct Store<float> {
+  __device__ static void four(void *base, size_t idx, float a, float b, float c, float d) {
+    *reinterpret_cast<float4 *>(static_cast<float *>(base) + idx) = make_float4(a, b, c, d);
+  }
+};
+template <> struct Store<__bf16> {
+  __device__ static void four(void *base, size_t idx, float a, float b, float c, float d) {
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    bf16x4 v = {(__bf16)a, (__bf16)b, (__bf16)c, (__bf16)d};  // round to nearest even
+    *reinterpret_cast<bf16x4 *>(static_cast<__bf16 *>(base) + idx) = v;
+  }
+};
+
+// out[b, head0 .. head0+nh-1, :] = 0 (a sequence with no cached positions).
+template <typename T, int D>
+__device__ void write_zero_heads(const DecodeParams &p, int b, int head0, int nh) {
+  for (int idx = threadIdx.x; idx < nh * (D / 4); idx += blockDim.x) {
+    const int j = idx / (D / 4), c = (idx % (D / 4)) * 4;
+    Store<T>::four(p.out, ((size_t)b * p.H + head0 + j) * D + c, 0.f, 0.f, 0.f, 0.f);
+  }
+}
+
+// Publishes this workgroup's partial (already stored by all threads) and
+// returns true in every thread of the workgroup that arrived last for its
+// counter; that workgroup then owns the merge.  The last arrival resets the
+// counter to zero, so the workspace is clear again when the kernel ends.
+__device__ __forceinline__ bool arrive_last(unsigned *counter, int nsplit) {
+  __shared__ int s_last;
+  __threadfence();  // release: this thread's partial stores reach device scope
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned prev = atomicAdd(counter, 1u);
+    const int last = prev == (unsigned)(nsplit - 1);
+    if (last) atomicExch(counter, 0u);
+    s_last = last;
+  }
+  __syncthreads();
+  const bool last = s_last != 0;
+  if (last) __threadfence();  // acquire: see every other split's partial
+  return last;
+}
+
+// Log-sum-exp merge of the nsplit partials of heads head0 .. head0+nh-1 of
+// sequence b into out.  Splits are visited in index order (deterministic).
+template <typename T, int D>
+__device__ void merge_splits(const DecodeParams &p, int b, int head0, int nh, int nsplit) {
+  for (int idx = threadIdx.x; idx < nh * (D / 4); idx += blockDim.x) {
+    const int j = idx / (D / 4), c = (idx % (D / 4)) * 4;
+    const size_t hs = ((size_t)b * p.H + head0 + j) * p.S;
+    float M = kNegInf;
+    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, p.ws_ml[hs + s].x);
+    const float sh = safe_shift(M);
+    float L = 0.f, o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+    for (int s = 0; s < nsplit; ++s) {
+      const float2 ml = p.ws_ml[hs + s];
+      const float a = fast_exp2(ml.x - sh);
+      const float4 o = *reinterpret_cast<const float4 *>(p.ws_o + (hs + s) * D + c);
+      L += ml.y * a;
+      o0 += o.x * a;
+      o1 += o.y * a;
+      o2 += o.z * a;
+      o3 += o.w * a;
+    }
+    const float inv = 1.f / L;
+    Store<T>::four(p.out, ((size_t)b * p.H + head0 + j) * D + c, o0 * inv, o1 * inv, o2 * inv, o3 * inv);
+  }
+}
+
+// Host-side launchers (one per kernel translation unit).
+hipError_t launch_decode_valu(const DecodeParams &p, int dtype, int D, int RC, unsigned grid, hipStream_t stream);
+hipError_t launch_decode_mfma(const DecodeParams &p, int D, int HB, unsigned grid, hipStream_t stream);
+hipError_t launch_meanpool(const float *w, int d_model, int H, int G, int h, float *w_out, hipStream_t stream);
+hipError_t launch_fill_zero(void *ptr, size_t bytes, hipStream_t stream);
+
+}  // namespace gqa

@@ -1,0 +1,138 @@
+/*
+ * gqa.h - grouped-query decode attention on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libgqa.so.  Plain pointers and sizes; device buffers are owned by
+ * the caller.  The library never allocates, frees or synchronises; every call
+ * only enqueues work on the given HIP stream and returns.
+ *
+ * What is computed (sources are the public pages on grouped-query attention,
+ * cited by title and section):
+ *   wikillm "Grouped-query attention (GQA)", Overview and Implementation
+ *   sketch (decode-step block): the H query heads form G groups; each query
+ *   head attends with its group's single key head and value head over every
+ *   cached position:
+ *       out[b,h,:] = sum_t softmax_t( scale * q[b,h,:] . K[b,g,t,:] ) * V[b,g,t,:]
+ *   with g = h / (H/G) - the block assignment of consecutive query heads to a
+ *   group that the sketch assumes (the paper does not state it).
+ *   elemedex glossary "grouped-query attention", paragraph "Grouped (GQA)":
+ *   G = 1 is multi-query attention, G = H is multi-head attention; both are
+ *   ordinary calls of the same entry point.
+ *
+ * Conventions shared by all entry points:
+ *   - Tensors are dense, row-major, contiguous; element type per gqa_dtype.
+ *   - Argument errors are reported on the host, before anything is enqueued.
+ *   - GQA_ERR_HIP means a HIP launch or runtime call failed; the HIP error
+ *     text is available from gqa_last_hip_error().
+ *   - Nothing throws across the ABI.  Calls are reentrant; two calls that
+ *     share one workspace must not overlap in time (use one stream).
+ */
+#ifndef GQA_H_
+#define GQA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GQA_F32 = 0,  /* IEEE binary32 */
+  GQA_BF16 = 1  /* bfloat16: the upper 16 bits of a binary32 */
+} gqa_dtype;
+
+typedef enum {
+  GQA_OK = 0,
+  GQA_ERR_NULL = 1,        /* a required pointer is NULL */
+  GQA_ERR_SHAPE = 2,       /* a size is negative, H, G, d or Lmax < 1, or H % G != 0 */
+  GQA_ERR_UNSUPPORTED = 3, /* d not in {64, 128} (or h < 1 for meanpool), unknown dtype */
+  GQA_ERR_ALIGN = 4,       /* q, k_cache, v_cache or out not 16-byte aligned; workspace not 256-byte aligned */
+  GQA_ERR_WORKSPACE = 5,   /* workspace_bytes < gqa_decode_workspace_size(...) */
+  GQA_ERR_SCALE = 6,       /* scale is NaN or infinite */
+  GQA_ERR_HIP = 7,         /* a HIP call failed */
+  GQA_ERR_SIZE = 8         /* a size product overflows the supported index range */
+} gqa_status;
+
+/*
+ * Bytes of device workspace that gqa_decode needs for this shape (0 when it
+ * needs none).  The workspace holds per-split partial results and per-(b,g)
+ * arrival counters.  Returns 0 for arguments gqa_decode would reject.
+ */
+size_t gqa_decode_workspace_size(int B, int H, int G, int d, int Lmax, gqa_dtype dtype);
+
+/*
+ * Clears a workspace before its first use (enqueues a fill kernel on
+ * `stream`).  Equivalent to filling the buffer with zero bytes.  After a
+ * completed gqa_decode call the workspace is again in this cleared state, so
+ * one workspace serves any number of sequential calls of any shape whose
+ * requirement it meets.
+ */
+gqa_status gqa_workspace_init(void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Grouped-query decode attention for one new token per sequence.
+ *
+ *   q         [B, H, d]        dtype, device.  Query heads of the new token.
+ *   k_cache   [B, G, Lmax, d]  dtype, device.  Key cache; K/V head g of
+ *   v_cache   [B, G, Lmax, d]  sequence b is one contiguous Lmax*d slab.
+ *   seq_lens  [B] int32, device.  Positions 0 .. seq_lens[b]-1 are attended;
+ *             the new token's key/value must already be in the cache (the
+ *             sketch appends before attending).  Values are clamped to
+ *             [0, Lmax] on the device; 0 gives out[b] = 0.  Positions at or
+ *             beyond seq_lens[b] are never read.
+ *   B, H, G, d, Lmax  B >= 0 (B = 0 is a no-op; pointers are then not
+ *             checked), H >= 1, G >= 1, H % G == 0, d in {64, 128}, Lmax >= 1.
+ *   scale     multiplies q . k before the softmax (1/sqrt(d) in the pages'
+ *             sketch); must be finite.
+ *   dtype     element type of q, k_cache, v_cache and out.
+ *   out       [B, H, d] dtype, device.  Must not alias the inputs.  Rounded
+ *             once (to nearest even) from binary32 accumulation.
+ *   workspace device buffer of workspace_bytes >= gqa_decode_workspace_size
+ *             (may be NULL when that size is 0), 256-byte aligned, cleared
+ *             once by gqa_workspace_init (or any zero fill) before first use.
+ *   stream    HIP stream the work is enqueued on (NULL: the null stream).
+ *
+ * NaN or Inf inside the attended positions propagate to the output.
+ */
+gqa_status gqa_decode(const void *q, const void *k_cache, const void *v_cache, const int32_t *seq_lens,
+                      int B, int H, int G, int d, int Lmax, float scale, gqa_dtype dtype, void *out,
+                      void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The pages' checkpoint conversion step, numeric core only: wikillm
+ * "Grouped-query attention (GQA)", Implementation sketch (conversion block)
+ * and Variants ("Converted and uptrained checkpoints"): the key (or value)
+ * projection columns of the H/G heads of each group are mean-pooled.
+ *
+ *   w      [d_model, H*h] binary32, device; head i owns columns i*h .. (i+1)*h-1.
+ *   w_out  [d_model, G*h] binary32, device; column block g is the mean of the
+ *          blocks of heads g*r .. g*r+r-1, r = H/G (block assignment).
+ *
+ * Arithmetic (bit-exact, deterministic): binary64 sum of the members in
+ * ascending head order starting from the first member, one binary64 division
+ * by r, one rounding to binary32 (nearest even).  Call once for W_K and once
+ * for W_V; W_Q and W_O are left as they are.  d_model = 0 is a no-op.
+ */
+gqa_status gqa_meanpool_kv(const float *w, int d_model, int H, int G, int h, float *w_out, hipStream_t stream);
+
+/* Static description of a status code. */
+const char *gqa_status_string(gqa_status status);
+
+/* Text of the HIP error behind the last GQA_ERR_HIP in this thread ("" if none). */
+const char *gqa_last_hip_error(void);
+
+/*
+ * Which decode kernel a shape runs on: 0 = VALU kernel (binary32 or bfloat16
+ * dot products on the vector ALUs), 1 = MFMA kernel (bfloat16 matrix cores).
+ * Returns -1 for arguments gqa_decode would reject.  Selection can be forced
+ * with the environment variable GQA_KERNEL=valu|mfma (bfloat16 only for mfma).
+ */
+int gqa_decode_kernel_kind(int B, int H, int G, int d, int Lmax, gqa_dtype dtype);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_H_ */

@@ -1,0 +1,165 @@
+"""The C ABI without a GPU: the library loads, exports what include/gqa.h
+declares, and rejects bad arguments on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import grouped_query_kv_decode_amd as gqa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gqa.h")
+
+OK, NULL, SHAPE, UNSUP, ALIGN, WS, SCALE, HIP, SIZE = range(9)
+F32, BF16 = 0, 1
+P = 0x10000  # a 256-byte aligned dummy address; never dereferenced on these paths
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return gqa.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gqa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_list():
+    assert declared_functions() == sorted(gqa.EXPORTED)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for s in range(9):
+        txt = gqa.status_string(s)
+        assert txt and txt != "unknown status"
+    assert gqa.status_string(99) == "unknown status"
+
+
+def decode(lib, q=P, k=P, v=P, lens=P, B=2, H=8, G=2, d=128, L=512, scale=0.125, dt=BF16, out=P, ws=P,
+           ws_bytes=1 << 30):
+    return lib.gqa_decode(q, k, v, lens, B, H, G, d, L, scale, dt, out, ws, ws_bytes, None)
+
+
+def test_shape_errors(lib):
+    assert decode(lib, H=6, G=4) == SHAPE
+    assert decode(lib, B=-1) == SHAPE
+    assert decode(lib, H=0) == SHAPE
+    assert decode(lib, G=0) == SHAPE
+    assert decode(lib, L=0) == SHAPE
+    assert decode(lib, d=0) == SHAPE
+
+
+def test_unsupported(lib):
+    assert decode(lib, d=96) == UNSUP
+    assert decode(lib, d=256) == UNSUP
+    assert decode(lib, dt=7) == UNSUP
+
+
+def test_empty_batch_is_a_noop(lib):
+    assert decode(lib, B=0, q=None, k=None, v=None, lens=None, out=None, ws=None, ws_bytes=0) == OK
+
+
+def test_null_pointers(lib):
+    for kw in ("q", "k", "v", "lens", "out"):
+        assert decode(lib, **{kw: None}) == NULL, kw
+
+
+def test_alignment(lib):
+    for kw in ("q", "k", "v", "out"):
+        assert decode(lib, **{kw: P + 8}) == ALIGN, kw
+    assert decode(lib, lens=P + 2) == ALIGN
+
+
+def test_scale(lib):
+    assert decode(lib, scale=float("nan")) == SCALE
+    assert decode(lib, scale=float("inf")) == SCALE
+    assert decode(lib, scale=3e38) == SCALE  # scale * log2(e) overflows binary32
+
+
+def test_workspace_checks(lib, monkeypatch):
+    monkeypatch.setenv("GQA_CHUNK", "128")
+    need = lib.gqa_decode_workspace_size(2, 8, 2, 128, 512, BF16)
+    assert need > 0
+    assert decode(lib, ws_bytes=need - 1) == WS
+    assert decode(lib, ws=None, ws_bytes=need) == NULL
+    assert decode(lib, ws=P + 16, ws_bytes=need) == ALIGN
+
+
+def test_workspace_size_model(lib, monkeypatch):
+    B, H, G, d, L = 2, 8, 2, 128, 512
+    monkeypatch.setenv("GQA_CHUNK", "128")
+    S = 4
+    need = lib.gqa_decode_workspace_size(B, H, G, d, L, BF16)
+    # partial outputs + (max, sum) pairs + counters, each region 256-byte aligned
+    assert need >= B * H * S * d * 4 + B * H * S * 8 + B * G * 4
+    assert need <= B * H * S * d * 4 + B * H * S * 8 + B * G * 4 + 2 * 256
+    monkeypatch.setenv("GQA_CHUNK", str(L))
+    assert lib.gqa_decode_workspace_size(B, H, G, d, L, BF16) == 0  # one split: no workspace
+    assert lib.gqa_decode_workspace_size(B, 6, 4, d, L, BF16) == 0  # rejected shape
+
+
+def test_kernel_selection(lib, monkeypatch):
+    monkeypatch.delenv("GQA_KERNEL", raising=False)
+    assert lib.gqa_decode_kernel_kind(16, 32, 8, 128, 4096, BF16) == 1
+    assert lib.gqa_decode_kernel_kind(1, 8, 2, 64, 256, F32) == 0
+    assert lib.gqa_decode_kernel_kind(1, 128, 1, 64, 256, BF16) == 0  # more than 64 heads per group
+    assert lib.gqa_decode_kernel_kind(1, 6, 4, 64, 256, BF16) == -1
+    monkeypatch.setenv("GQA_KERNEL", "valu")
+    assert lib.gqa_decode_kernel_kind(16, 32, 8, 128, 4096, BF16) == 0
+
+
+def test_meanpool_argument_errors(lib):
+    mp = lib.gqa_meanpool_kv
+    assert mp(P, 16, 6, 4, 8, P, None) == SHAPE
+    assert mp(P, -1, 8, 2, 8, P, None) == SHAPE
+    assert mp(P, 16, 8, 2, 0, P, None) == UNSUP
+    assert mp(None, 0, 8, 2, 8, None, None) == OK
+    assert mp(None, 16, 8, 2, 8, P, None) == NULL
+    assert mp(P, 16, 8, 2, 8, None, None) == NULL
+    assert mp(P + 2, 16, 8, 2, 8, P, None) == ALIGN
+
+
+def test_workspace_init_arguments(lib):
+    assert lib.gqa_workspace_init(None, 0, None) == OK
+    assert lib.gqa_workspace_init(None, 64, None) == NULL
+
+
+def test_binding_rejects_bad_tensors():
+    import torch
+    q = torch.zeros(2, 8, 64)
+    k = torch.zeros(2, 2, 16, 64)
+    with pytest.raises(ValueError):
+        gqa.decode(q, k, k, torch.zeros(2, dtype=torch.int32), 0.1)  # CPU tensors
+    with pytest.raises(TypeError):
+        gqa.decode(q, k, k, torch.zeros(2, dtype=torch.int64), 0.1)
+    with pytest.raises(ValueError):
+        gqa.decode(q, k[:1], k[:1], torch.zeros(2, dtype=torch.int32), 0.1)
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(RuntimeError):
+        gqa.load_library(str(tmp_path / "libgqa.so"))
+
+
+def test_oracle_and_product_are_independent():
+    """Neither side imports, includes or links the other."""
+    pkg = os.path.join(ROOT, "grouped_query_kv_decode_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", text, re.M), f
+                assert "gqa_oracle" not in text, f
+    for f in os.listdir(os.path.join(ROOT, "oracle")):
+        if f.endswith((".py", ".c", ".h")):
+            text = open(os.path.join(ROOT, "oracle", f)).read()
+            assert "grouped_query_kv_decode_amd" not in text, f
+            assert "gqa.h" not in text, f

@@ -1,0 +1,246 @@
+"""HIP path (through the C ABI) against the CPU oracle, on the GPU.
+
+Tolerances: max |gpu - oracle| <= 1e-5 for float32 inputs and <= 2e-2 for
+bfloat16 inputs (binary32 accumulation, one rounding of the output; the
+oracle reads the same rounded inputs in binary64).  The mean-pool helper must
+match bit for bit.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import grouped_query_kv_decode_amd as gqa
+from grouped_query_kv_decode_amd import workloads as wl
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 2e-2}
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a visible GPU")
+    gqa.load_library()
+    yield
+
+
+@pytest.fixture
+def env(monkeypatch):
+    """Set launch-plan environment overrides for one test."""
+    def set_(**kw):
+        for k, v in kw.items():
+            if v is None:
+                monkeypatch.delenv(k, raising=False)
+            else:
+                monkeypatch.setenv(k, str(v))
+    set_(GQA_KERNEL=None, GQA_CHUNK=None, GQA_TARGET_WGS=None, GQA_MAX_CHUNK=None)
+    return set_
+
+
+def run_gpu(q, k, v, lens, scale):
+    out = gqa.decode(q, k, v, lens, scale)
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_out(q, k, v, lens, scale, rows=None):
+    """Oracle on the host copies; rows = optional list of sequences to compute."""
+    if rows is None:
+        return oracle.decode(q.cpu(), k.cpu(), v.cpu(), lens.cpu(), scale)
+    outs = []
+    for b in rows:
+        n = max(1, min(int(lens[b]), k.shape[2]))
+        outs.append(oracle.decode(q[b:b + 1].cpu(), k[b:b + 1, :, :n].cpu(), v[b:b + 1, :, :n].cpu(),
+                                  lens[b:b + 1].cpu(), scale)[0])
+    return np.stack(outs)
+
+
+def check(out, ref, dtype, what=""):
+    got = out.detach().float().cpu().double().numpy()
+    assert got.shape == ref.shape
+    assert np.all(np.isfinite(got)), what + ": non-finite output"
+    err = float(np.max(np.abs(got - ref))) if got.size else 0.0
+    print("%s max|err| = %.3g (max|out| = %.3g)" % (what, err, float(np.max(np.abs(ref))) if ref.size else 0.0))
+    assert err <= TOL[dtype], "%s: max|err| %.3g > %.3g" % (what, err, TOL[dtype])
+    return err
+
+
+def rand_case(B, H, G, d, Lmax, lens, dtype, seed, scale=None, value_scale=1.0):
+    w = wl.Workload("case", B, H, G, d, Lmax, dtype, seed, value_scale=value_scale)
+    q, k, v, _ = wl.make_inputs(w, DEV, pad="nan", seq_lens=torch.tensor(lens, dtype=torch.int32))
+    lens_t = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    return q, k, v, lens_t, (w.scale if scale is None else scale)
+
+
+# --------------------------------------------------------------- small shapes, every path
+
+SMALL = [
+    # (B, H, G, d, Lmax, lens)
+    (1, 8, 2, 64, 256, [256]),
+    (3, 8, 2, 128, 600, [600, 1, 333]),
+    (2, 32, 8, 128, 1000, [1000, 517]),
+    (4, 12, 4, 64, 300, [129, 128, 127, 31]),     # r = 3
+    (2, 16, 16, 128, 700, [700, 65]),             # G = H (MHA)
+    (2, 16, 1, 64, 400, [400, 97]),               # G = 1 (MQA), r = 16
+    (2, 24, 1, 128, 300, [300, 33]),              # r = 24 (two head blocks)
+    (2, 64, 1, 64, 260, [260, 200]),              # r = 64 (four head blocks)
+    (2, 64, 8, 64, 520, [520, 7]),                # r = 8
+    (2, 6, 3, 128, 90, [90, 45]),                 # r = 2, less than one tile per wave
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "B%d_H%d_G%d_d%d_L%d" % c[:5])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("kernel", ["default", "valu"])
+@pytest.mark.parametrize("chunk", [None, 128, 100000])
+def test_small_parity(env, case, dtype, kernel, chunk):
+    B, H, G, d, L, lens = case
+    env(GQA_KERNEL=None if kernel == "default" else kernel, GQA_CHUNK=chunk)
+    q, k, v, lens_t, scale = rand_case(B, H, G, d, L, lens, dtype, seed=sum(case[:5]) + 7 * len(lens))
+    out = run_gpu(q, k, v, lens_t, scale)
+    check(out, oracle_out(q, k, v, lens_t, scale), dtype, "%s %s chunk=%s %s" % (dtype, kernel, chunk, case))
+
+
+def test_tiny_workload_fp32(env):
+    w = wl.TINY_F32
+    q, k, v, lens = wl.make_inputs(w, DEV)
+    out = run_gpu(q, k, v, lens, w.scale)
+    check(out, oracle_out(q, k, v, lens, w.scale), "f32", w.name)
+
+
+# --------------------------------------------------------------- edge cases
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_empty_and_clamped_lengths(env, dtype):
+    env(GQA_CHUNK=128)
+    q, k, v, _, scale = rand_case(3, 8, 2, 128, 300, [300, 300, 300], dtype, seed=5)
+    lens = torch.tensor([0, 1000, 1], dtype=torch.int32, device=DEV)
+    out = run_gpu(q, k, v, lens, scale)
+    assert torch.all(out[0] == 0)
+    ref = oracle_out(q, k, v, lens, scale)
+    check(out, ref, dtype, "len 0 / >Lmax / 1")
+    # one position: the output is that value row, rounded once
+    for h in range(8):
+        assert torch.equal(out[2, h], v[2, h // 4, 0])
+
+
+def test_empty_batch(env):
+    q = torch.empty((0, 8, 64), dtype=torch.bfloat16, device=DEV)
+    k = torch.empty((0, 2, 16, 64), dtype=torch.bfloat16, device=DEV)
+    out = gqa.decode(q, k, k, torch.empty((0,), dtype=torch.int32, device=DEV), 0.125)
+    assert out.shape == (0, 8, 64)
+
+
+@pytest.mark.parametrize("kernel", ["default", "valu"])
+def test_split_boundaries(env, kernel):
+    """Lengths at chunk and tile boundaries +-1 with several splits."""
+    env(GQA_KERNEL=None if kernel == "default" else kernel, GQA_CHUNK=256)
+    lens = [255, 256, 257, 511, 512, 513, 31, 32, 33, 1]
+    q, k, v, lens_t, scale = rand_case(len(lens), 32, 8, 128, 520, lens, "bf16", seed=77)
+    out = run_gpu(q, k, v, lens_t, scale)
+    check(out, oracle_out(q, k, v, lens_t, scale), "bf16", "split boundaries " + kernel)
+
+
+def test_large_scores_stay_finite(env):
+    q, k, v, lens, scale = rand_case(2, 16, 4, 128, 700, [700, 300], "bf16", seed=8)
+    q.mul_(8)
+    k.mul_(8)
+    out = run_gpu(q, k, v, lens, scale)
+    check(out, oracle_out(q, k, v, lens, scale), "bf16", "large scores")
+
+
+def test_nan_inside_valid_positions_propagates(env):
+    env(GQA_CHUNK=128)
+    q, k, v, lens, scale = rand_case(2, 8, 2, 128, 300, [300, 300], "bf16", seed=9)
+    k[0, 1, 17, 5] = float("nan")
+    out = run_gpu(q, k, v, lens, scale).float().cpu()
+    ref = oracle_out(q, k, v, lens, scale)
+    assert np.array_equal(np.isnan(out.numpy()), np.isnan(ref))
+    assert torch.isnan(out[0, 4:]).all() and not torch.isnan(out[0, :4]).any() and not torch.isnan(out[1]).any()
+
+
+def test_deterministic_and_workspace_reuse(env):
+    env(GQA_CHUNK=128)
+    a = rand_case(3, 32, 8, 128, 900, [900, 400, 129], "bf16", seed=10)
+    b = rand_case(5, 16, 2, 64, 300, [300, 1, 2, 299, 150], "bf16", seed=11)
+    o1 = run_gpu(*a).clone()
+    o2 = run_gpu(*b).clone()
+    o3 = run_gpu(*a).clone()
+    assert torch.equal(o1, o3)
+    check(o2, oracle_out(*b), "bf16", "second shape")
+    check(o3, oracle_out(*a), "bf16", "reuse")
+
+
+def test_non_default_stream(env):
+    env(GQA_CHUNK=128)
+    q, k, v, lens, scale = rand_case(2, 32, 8, 128, 640, [640, 300], "bf16", seed=12)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        out = gqa.decode(q, k, v, lens, scale)
+    s.synchronize()
+    check(out, oracle_out(q, k, v, lens, scale), "bf16", "side stream")
+
+
+def test_equal_queries_in_a_group(env):
+    q, k, v, lens, scale = rand_case(1, 16, 4, 128, 500, [500], "bf16", seed=13)
+    q[0, 4:8] = q[0, 4]
+    out = run_gpu(q, k, v, lens, scale)
+    for h in range(4, 8):
+        assert torch.equal(out[0, h], out[0, 4])
+
+
+def test_outlier_rows_alternative_reading(env):
+    """Second reading of the Gemma-shaped outlier recipe: 1% of K rows x20."""
+    q, k, v, lens, scale = rand_case(2, 32, 16, 128, 2048, [2048, 1500], "bf16", seed=14)
+    gen = torch.Generator(DEV).manual_seed(14)
+    rows = torch.rand(k.shape[:3], generator=gen, device=DEV) < 0.01
+    k[rows] = (k[rows].float() * 20).to(k.dtype)
+    out = run_gpu(q, k, v, lens, scale)
+    check(out, oracle_out(q, k, v, lens, scale), "bf16", "outlier rows")
+
+
+# --------------------------------------------------------------- the named workloads at full size
+
+FULL = [wl.MISTRAL_7B, wl.GEMMA2_27B] + [wl.t5xxl_sweep(g) for g in wl.T5XXL_SWEEP_G]
+
+
+@pytest.mark.parametrize("w", FULL, ids=lambda w: w.name)
+def test_full_workload(env, w):
+    q, k, v, lens = wl.make_inputs(w, DEV)
+    out = run_gpu(q, k, v, lens, w.scale)
+    check(out, oracle_out(q, k, v, lens, w.scale), w.dtype, w.name)
+
+
+def test_ragged_workload_sampled(env):
+    """Ragged long-context workload at full size; the oracle checks a sample of
+    sequences (the shortest, the longest and a few more) one by one."""
+    w = wl.RAGGED
+    q, k, v, lens = wl.make_inputs(w, DEV)
+    out = run_gpu(q, k, v, lens, w.scale)
+    lc = lens.cpu()
+    rows = sorted({int(lc.argmin()), int(lc.argmax()), 0, 17, 42, w.B - 1})
+    ref = oracle_out(q, k, v, lens, w.scale, rows=rows)
+    check(out[rows], ref, w.dtype, w.name + " sampled")
+    assert torch.isfinite(out.float()).all()
+
+
+# --------------------------------------------------------------- mean-pool conversion
+
+@pytest.mark.parametrize("shape", [(4096, 32, 8, 128), (512, 12, 4, 64), (256, 8, 8, 128), (300, 8, 1, 96),
+                                   (1, 3, 1, 1)])
+def test_meanpool_bit_exact(shape):
+    d_model, H, G, h = shape
+    gen = torch.Generator("cpu").manual_seed(d_model + H)
+    w = torch.randn((d_model, H * h), generator=gen) * torch.exp(torch.randn((d_model, H * h), generator=gen) * 3)
+    w[0, :min(4, H * h)] = -0.0
+    got = gqa.meanpool_kv(w.to(DEV), H, G).cpu()
+    torch.cuda.synchronize()
+    ref = oracle.meanpool(w.numpy(), H, G)
+    assert np.array_equal(got.numpy().view(np.uint32), ref.view(np.uint32))
