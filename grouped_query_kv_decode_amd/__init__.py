@@ -8,6 +8,7 @@ fallback path.  PyTorch supplies device memory and the stream.
 Entry points (same names as the C ABI, without the ``gqa_`` prefix):
     decode(q, k_cache, v_cache, seq_lens, scale, out=None, workspace=None)
     decode_workspace_size(B, H, G, d, Lmax, dtype)
+    decode_phase(phase, ...)           (split kernel / merge kernel separately)
     workspace_init(workspace)
     meanpool_kv(w, H, G, out=None)
     decode_kernel_kind(B, H, G, d, Lmax, dtype)
@@ -18,7 +19,7 @@ import ctypes
 import os
 
 __all__ = [
-    "GQAError", "decode", "decode_workspace_size", "workspace_init", "meanpool_kv",
+    "GQAError", "decode", "decode_phase", "decode_workspace_size", "workspace_init", "meanpool_kv",
     "decode_kernel_kind", "status_string", "library_path", "load_library", "Decoder",
     "GQA_F32", "GQA_BF16",
 ]
@@ -32,7 +33,7 @@ STATUS_NAMES = {
     5: "GQA_ERR_WORKSPACE", 6: "GQA_ERR_SCALE", 7: "GQA_ERR_HIP", 8: "GQA_ERR_SIZE",
 }
 EXPORTED = [
-    "gqa_decode_workspace_size", "gqa_workspace_init", "gqa_decode", "gqa_meanpool_kv",
+    "gqa_decode_workspace_size", "gqa_workspace_init", "gqa_decode", "gqa_decode_phase", "gqa_meanpool_kv",
     "gqa_status_string", "gqa_last_hip_error", "gqa_decode_kernel_kind",
 ]
 
@@ -66,6 +67,8 @@ def load_library(path: str | None = None):
     lib.gqa_decode_workspace_size.argtypes = [ci, ci, ci, ci, ci, ci]
     lib.gqa_workspace_init.restype = ci
     lib.gqa_workspace_init.argtypes = [vp, sz, vp]
+    lib.gqa_decode_phase.restype = ci
+    lib.gqa_decode_phase.argtypes = [ci, vp, vp, vp, vp, ci, ci, ci, ci, ci, ctypes.c_float, ci, vp, vp, sz, vp]
     lib.gqa_decode.restype = ci
     lib.gqa_decode.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, ci, ctypes.c_float, ci, vp, vp, sz, vp]
     lib.gqa_meanpool_kv.restype = ci
@@ -110,6 +113,7 @@ def decode_kernel_kind(B, H, G, d, Lmax, dtype) -> int:
 
 
 def workspace_init(workspace) -> None:
+    """Clear a workspace (uint8 tensor) before its first use."""
     st = load_library().gqa_workspace_init(workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                            _stream_handle(workspace.device))
     if st:
@@ -125,7 +129,8 @@ def _workspace_for(nbytes: int, device):
     key = (device.index, _stream_handle(device))
     ws = _ws_cache.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        workspace_init(ws)
         _ws_cache[key] = ws
     return ws
 
@@ -175,6 +180,15 @@ def decode(q, k_cache, v_cache, seq_lens, scale: float, out=None, workspace=None
     return out
 
 
+def decode_phase(phase: int, q, k_cache, v_cache, seq_lens, scale: float, out=None, workspace=None):
+    """One phase of decode (1: split kernel, 2: merge kernel, 0: both); see gqa.h."""
+    args, out, _ = _prepare(q, k_cache, v_cache, seq_lens, scale, out, workspace)
+    st = load_library().gqa_decode_phase(int(phase), *args, _stream_handle(q.device))
+    if st:
+        raise GQAError(st, "gqa_decode_phase")
+    return out
+
+
 class Decoder:
     """A decode call bound to fixed tensors and to the stream current at
     construction; each call() is one C-ABI call with pre-marshalled
@@ -185,11 +199,18 @@ class Decoder:
         self._args, self.out, self.workspace = _prepare(q, k_cache, v_cache, seq_lens, scale, out, workspace)
         self._args = self._args + (_stream_handle(q.device),)
         self._fn = load_library().gqa_decode
+        self._phase = load_library().gqa_decode_phase
 
     def __call__(self):
         st = self._fn(*self._args)
         if st:
             raise GQAError(st, "gqa_decode")
+        return self.out
+
+    def phase(self, phase: int):
+        st = self._phase(phase, *self._args)
+        if st:
+            raise GQAError(st, "gqa_decode_phase")
         return self.out
 
 

@@ -31,8 +31,11 @@ COMMON = [
 
 # (source, extra flags)
 SOURCES = [
-    ("gqa_decode_mfma.hip", []),
+    # keep MFMA accumulators in VGPRs: the softmax rescale then needs no
+    # AGPR<->VGPR copies in the streaming loop
+    ("gqa_decode_mfma.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]),
     ("gqa_decode_valu.hip", []),
+    ("gqa_merge.hip", []),
     # bit-exact conversion arithmetic: no contraction of any kind
     ("gqa_meanpool.hip", ["-ffp-contract=off"]),
     ("gqa_api.hip", []),

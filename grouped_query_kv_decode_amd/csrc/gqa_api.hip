@@ -36,11 +36,22 @@ int next_pow2(int x) {
 
 enum { KIND_VALU = 0, KIND_MFMA = 1 };
 
+// Workspace layout when some sequence may span several splits:
+//   [0, kCounterBytes)  arrival counters, one per (b, g, head chunk) unit;
+//                       zero between calls (each call leaves them zero)
+//   ml region           float2 [B, H, S]   split (max, weight sum)
+//   o region            float  [B, H, S, d] split un-normalised outputs
+// The counter region is never used for anything else, whatever the shape,
+// so one cleared workspace serves calls of any shape.
+constexpr size_t kCounterBytes = 256 * 1024;
+constexpr long kMaxFusedUnits = kCounterBytes / sizeof(unsigned);
+
 struct Plan {
   int kind;
   int chunk, S, HC, RC, HB;
+  int fused;
   unsigned grid;
-  size_t cnt_off, ml_off, o_off, ws_bytes;
+  size_t ml_off, o_off, ws_bytes;
 };
 
 gqa_status check_shape(int B, int H, int G, int d, int Lmax, gqa_dtype dt) {
@@ -53,6 +64,9 @@ gqa_status check_shape(int B, int H, int G, int d, int Lmax, gqa_dtype dt) {
 // Decode launch plan.  One workgroup per (b, g, head chunk, split); splits
 // are sized so that the grid holds about GQA_TARGET_WGS workgroups (default
 // 2048, eight per compute unit) with at most GQA_MAX_CHUNK positions each.
+// When a sequence spans several splits, the workgroup that finishes its
+// (b, g) unit last merges the partials inside the same kernel; with more
+// units than counters (or GQA_MERGE=kernel) a second kernel merges instead.
 gqa_status make_plan(int B, int H, int G, int d, int Lmax, gqa_dtype dt, Plan *pl) {
   const int r = H / G;
   const char *force = getenv("GQA_KERNEL");
@@ -86,13 +100,14 @@ gqa_status make_plan(int B, int H, int G, int d, int Lmax, gqa_dtype dt, Plan *p
   const unsigned long long grid = (unsigned long long)units * pl->S;
   if (grid == 0 || grid > 0x7fffffffULL) return GQA_ERR_SIZE;
   pl->grid = (unsigned)grid;
+  const char *merge = getenv("GQA_MERGE");
+  pl->fused = units <= kMaxFusedUnits && !(merge && strcmp(merge, "kernel") == 0);
   if (pl->S > 1) {
-    pl->cnt_off = 0;
-    pl->ml_off = round_up((size_t)units * sizeof(unsigned), 256);
+    pl->ml_off = kCounterBytes;
     pl->o_off = pl->ml_off + round_up((size_t)B * H * pl->S * sizeof(float2), 256);
     pl->ws_bytes = pl->o_off + (size_t)B * H * pl->S * d * sizeof(float);
   } else {
-    pl->cnt_off = pl->ml_off = pl->o_off = pl->ws_bytes = 0;
+    pl->ml_off = pl->o_off = pl->ws_bytes = 0;
   }
   return GQA_OK;
 }
@@ -124,9 +139,10 @@ gqa_status gqa_workspace_init(void *workspace, size_t workspace_bytes, hipStream
   return e == hipSuccess ? GQA_OK : hip_fail(e);
 }
 
-gqa_status gqa_decode(const void *q, const void *k_cache, const void *v_cache, const int32_t *seq_lens, int B, int H,
-                      int G, int d, int Lmax, float scale, gqa_dtype dtype, void *out, void *workspace,
-                      size_t workspace_bytes, hipStream_t stream) {
+gqa_status gqa_decode_phase(int phase, const void *q, const void *k_cache, const void *v_cache,
+                            const int32_t *seq_lens, int B, int H, int G, int d, int Lmax, float scale,
+                            gqa_dtype dtype, void *out, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (phase != 0 && phase != 1 && phase != 2) return GQA_ERR_UNSUPPORTED;
   gqa_status st = check_shape(B, H, G, d, Lmax, dtype);
   if (st != GQA_OK) return st;
   if (B == 0) return GQA_OK;
@@ -151,9 +167,10 @@ gqa_status gqa_decode(const void *q, const void *k_cache, const void *v_cache, c
   p.seq_lens = seq_lens;
   p.out = out;
   char *ws = static_cast<char *>(workspace);
-  p.ws_cnt = pl.ws_bytes ? reinterpret_cast<unsigned *>(ws + pl.cnt_off) : nullptr;
+  p.ws_cnt = pl.ws_bytes ? reinterpret_cast<unsigned *>(ws) : nullptr;
   p.ws_ml = pl.ws_bytes ? reinterpret_cast<float2 *>(ws + pl.ml_off) : nullptr;
   p.ws_o = pl.ws_bytes ? reinterpret_cast<float *>(ws + pl.o_off) : nullptr;
+  p.fused = pl.fused;
   p.B = B;
   p.H = H;
   p.G = G;
@@ -164,9 +181,24 @@ gqa_status gqa_decode(const void *q, const void *k_cache, const void *v_cache, c
   p.HC = pl.HC;
   p.scale_log2 = (float)sl2;
 
-  const hipError_t e = pl.kind == KIND_MFMA ? gqa::launch_decode_mfma(p, d, pl.HB, pl.grid, stream)
-                                            : gqa::launch_decode_valu(p, (int)dtype, d, pl.RC, pl.grid, stream);
-  return e == hipSuccess ? GQA_OK : hip_fail(e);
+  if (phase != 2) {
+    const hipError_t e = pl.kind == KIND_MFMA ? gqa::launch_decode_mfma(p, d, pl.HB, pl.grid, stream)
+                                              : gqa::launch_decode_valu(p, (int)dtype, d, pl.RC, pl.grid, stream);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  if (phase != 1 && pl.S > 1 && !pl.fused) {
+    // one merge workgroup per (sequence, K/V head): all r heads of the group
+    const hipError_t e = gqa::launch_merge(p, (int)dtype, d, p.r, stream);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  return GQA_OK;
+}
+
+gqa_status gqa_decode(const void *q, const void *k_cache, const void *v_cache, const int32_t *seq_lens, int B, int H,
+                      int G, int d, int Lmax, float scale, gqa_dtype dtype, void *out, void *workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+  return gqa_decode_phase(0, q, k_cache, v_cache, seq_lens, B, H, G, d, Lmax, scale, dtype, out, workspace,
+                          workspace_bytes, stream);
 }
 
 gqa_status gqa_meanpool_kv(const float *w, int d_model, int H, int G, int h, float *w_out, hipStream_t stream) {

@@ -113,8 +113,13 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeParams p) {
   }
 
   const size_t slab = ((size_t)b * p.G + g) * (size_t)p.Lmax * D;
-  const __bf16 *kp = static_cast<const __bf16 *>(p.k) + slab + 8 * c;
-  const __bf16 *vp = static_cast<const __bf16 *>(p.v) + slab + (D == 128 ? 8 : 4) * nn;
+  const __bf16 *kbase = static_cast<const __bf16 *>(p.k) + slab;
+  const __bf16 *vbase = static_cast<const __bf16 *>(p.v) + slab;
+  // Lane offsets inside a tile (elements): K row of score half 0 (half 1 is
+  // 4 rows further), dims 8c..; V row 8c, dims VPL*nn ..
+  constexpr int VPL = D == 128 ? 8 : 4;
+  const int koff = (8 * (nn >> 2) + (nn & 3)) * D + 8 * c;
+  const int voff = 8 * c * D + VPL * nn;
 
   f32x4 o[HB][DB];
   float m[HB], l[HB];
@@ -126,23 +131,46 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeParams p) {
     for (int db = 0; db < DB; ++db) o[hb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  for (int tt = t0 + 32 * wave; tt < t1; tt += 128) {
-    // K rows for the two score halves, V rows 8c .. 8c+7 of the tile.
+  // One 32-position tile: K rows for the two score halves, V rows 8c .. 8c+7.
+  struct Tile {
     u32x4 kA[2][KB];
+    VRow vR[8];
+  };
+  // A whole tile inside the split: tile base is uniform, lane offsets fixed.
+  auto load_full = [&](Tile &T, int tt) {
+    const __bf16 *kt = kbase + (size_t)tt * D;
+    const __bf16 *vt = vbase + (size_t)tt * D;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+        T.kA[h][kb] = *reinterpret_cast<const u32x4 *>(kt + koff + h * 4 * D + kb * 32);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) T.vR[u] = *reinterpret_cast<const VRow *>(vt + voff + u * D);
+  };
+  // The last tile of a split: rows past the split end are clamped to its last
+  // row (never past the sequence length) and masked out of the softmax.
+  auto load_tail = [&](Tile &T, int tt) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int t = tt + 8 * (nn >> 2) + 4 * h + (nn & 3);
       const size_t row = (size_t)min(t, t1 - 1);
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) kA[h][kb] = *reinterpret_cast<const u32x4 *>(kp + row * D + kb * 32);
+      for (int kb = 0; kb < KB; ++kb)
+        T.kA[h][kb] = *reinterpret_cast<const u32x4 *>(kbase + row * D + 8 * c + kb * 32);
     }
-    VRow vR[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const size_t row = (size_t)min(tt + 8 * c + u, t1 - 1);
-      vR[u] = *reinterpret_cast<const VRow *>(vp + row * D);
+      T.vR[u] = *reinterpret_cast<const VRow *>(vbase + row * D + VPL * nn);
     }
-
+  };
+  // Scores, softmax weights and the weighted V sum of one tile.  The running
+  // reference m only moves when a tile's maximum exceeds it by more than
+  // 2^kSlack (then o and l are rescaled), so weights stay below 2^kSlack and
+  // the accumulators are touched by the matrix cores only.
+  constexpr float kSlack = 10.f;
+  auto compute = [&](const Tile &T, int tt, bool tail) {
     u32x4 pB[HB];
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
@@ -151,32 +179,31 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeParams p) {
       for (int h = 0; h < 2; ++h) {
         acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) acc[h] = mfma(kA[h][kb], qB[hb][kb], acc[h]);
+        for (int kb = 0; kb < KB; ++kb) acc[h] = mfma(T.kA[h][kb], qB[hb][kb], acc[h]);
       }
       // lane (c, nn): scores of positions tt + 8c + u, u = 4h + i, head nn
       float sc[8];
-      float mt = kNegInf;
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const float x = acc[u >> 2][u & 3] * p.scale_log2;
-        sc[u] = tt + 8 * c + u < t1 ? x : kNegInf;
-        mt = fmaxf(mt, sc[u]);
+        sc[u] = acc[u >> 2][u & 3] * p.scale_log2;
+        if (tail && tt + 8 * c + u >= t1) sc[u] = kNegInf;
       }
+      float mt = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
       mt = group_max(mt);
-      const float mn = fmaxf(m[hb], mt);
-      const float sh = safe_shift(mn);
-      const float alpha = fast_exp2(m[hb] - sh);
-      m[hb] = mn;
-      float pv[8], sum = 0.f;
+      if (__builtin_amdgcn_ballot_w64(mt > m[hb] + kSlack)) {
+        const float mn = mt > m[hb] + kSlack ? mt : m[hb];
+        const float alpha = fast_exp2(m[hb] - safe_shift(mn));
+        m[hb] = mn;
+        l[hb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[hb][db] *= alpha;
+      }
+      const float sh = safe_shift(m[hb]);
+      float pv[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         pv[u] = fast_exp2(sc[u] - sh);
-        sum += pv[u];
-      }
-      l[hb] = l[hb] * alpha + sum;
-      if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db) o[hb][db] *= alpha;
+        l[hb] += pv[u];
       }
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -184,8 +211,19 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeParams p) {
         pB[hb][k] = __builtin_bit_cast(unsigned, t2);
       }
     }
+    pv_steps<0, DB, HB>(o, T.vR, pB);
+  };
 
-    pv_steps<0, DB, HB>(o, vR, pB);
+  // Each wave takes every fourth 32-position tile of the split.
+  for (int tt = t0 + 32 * wave; tt < t1; tt += 128) {
+    Tile T;
+    if (tt + 32 <= t1) {
+      load_full(T, tt);
+      compute(T, tt, false);
+    } else {
+      load_tail(T, tt);
+      compute(T, tt, true);
+    }
   }
 
   // Per-head weight sums: add the four lane groups.
@@ -245,13 +283,13 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeParams p) {
                           row[3] * inv);
     } else {
       const size_t hs = ((size_t)b * p.H + head0 + j) * p.S + s;
-      *reinterpret_cast<float4 *>(p.ws_o + hs * D + cc) = make_float4(row[0], row[1], row[2], row[3]);
-      if (cc == 0) p.ws_ml[hs] = make_float2(M, L);
+      store_partial4(p.ws_o + hs * D + cc, row[0], row[1], row[2], row[3]);
+      if (cc == 0) store_ml(p.ws_ml + hs, M, L);
     }
   }
-  if (nsplit == 1) return;
+  if (nsplit == 1 || !p.fused) return;
   if (!arrive_last(p.ws_cnt + (size_t)b * p.G + g, nsplit)) return;
-  merge_splits<__bf16, D>(p, b, head0, p.r, nsplit);
+  merge_heads<__bf16, D>(p, b, head0, p.r, nsplit);
 }
 
 template <int D, int HB>

@@ -225,14 +225,13 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeParams p) {
                      sm_o[j][c + 2] * inv, sm_o[j][c + 3] * inv);
     } else {
       const size_t hs = ((size_t)b * p.H + head0 + j) * p.S + s;
-      *reinterpret_cast<float4 *>(p.ws_o + hs * D + c) =
-          make_float4(sm_o[j][c], sm_o[j][c + 1], sm_o[j][c + 2], sm_o[j][c + 3]);
-      if (c == 0) p.ws_ml[hs] = make_float2(M, L);
+      store_partial4(p.ws_o + hs * D + c, sm_o[j][c], sm_o[j][c + 1], sm_o[j][c + 2], sm_o[j][c + 3]);
+      if (c == 0) store_ml(p.ws_ml + hs, M, L);
     }
   }
-  if (nsplit == 1) return;
+  if (nsplit == 1 || !p.fused) return;
   if (!arrive_last(p.ws_cnt + ((size_t)b * p.G + g) * p.HC + hc, nsplit)) return;
-  merge_splits<T, D>(p, b, head0, nh, nsplit);
+  merge_heads<T, D>(p, b, head0, nh, nsplit);
 }
 
 template <typename T, int D, int RC>

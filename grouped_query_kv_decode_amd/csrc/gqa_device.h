@@ -1,6 +1,5 @@
 // Device-side pieces shared by the decode kernels: launch parameters, the
-// split-partial format, the arrival counter protocol and the log-sum-exp merge
-// of split partials.
+// split-partial format, and the in-kernel merge of split partials.
 //
 // Decode semantics follow the decode-step block of the Implementation sketch
 // on the wikillm page "Grouped-query attention (GQA)": per query head, softmax
@@ -23,7 +22,8 @@ struct DecodeParams {
   void *out;               // [B, H, D]
   float *ws_o;             // [B, H, S, D]  un-normalised split outputs
   float2 *ws_ml;           // [B, H, S]     (running max in log2 units, sum of weights)
-  unsigned *ws_cnt;        // [B * G * HC]  arrival counters, zero between calls
+  unsigned *ws_cnt;        // arrival counter per unit; zero between calls
+  int fused;               // 1: the last split of a unit merges; 0: a merge kernel follows
   int B, H, G, Lmax;
   int r;                   // query heads per K/V head, H / G
   int S;                   // splits per (b, g) in the grid
@@ -71,46 +71,71 @@ __device__ void write_zero_heads(const DecodeParams &p, int b, int head0, int nh
   }
 }
 
-// Publishes this workgroup's partial (already stored by all threads) and
-// returns true in every thread of the workgroup that arrived last for its
-// counter; that workgroup then owns the merge.  The last arrival resets the
-// counter to zero, so the workspace is clear again when the kernel ends.
+// Split partials are written and read with device-scope (sc1) accesses: they
+// are coherent across the XCDs' L2 caches without a cache write-back, so the
+// arrival protocol below needs no release fence.
+__device__ __forceinline__ void store_partial4(float *dst, float a, float b, float c, float d) {
+  __hip_atomic_store(reinterpret_cast<unsigned long long *>(dst),
+                     (unsigned long long)__float_as_uint(a) | ((unsigned long long)__float_as_uint(b) << 32),
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(reinterpret_cast<unsigned long long *>(dst + 2),
+                     (unsigned long long)__float_as_uint(c) | ((unsigned long long)__float_as_uint(d) << 32),
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_ml(float2 *dst, float m, float l) {
+  __hip_atomic_store(reinterpret_cast<unsigned long long *>(dst),
+                     (unsigned long long)__float_as_uint(m) | ((unsigned long long)__float_as_uint(l) << 32),
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 load_pair(const float *src) {
+  const unsigned long long v = __hip_atomic_load(reinterpret_cast<const unsigned long long *>(src), __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float((unsigned)v), __uint_as_float((unsigned)(v >> 32)));
+}
+
+// Called by every thread of a workgroup after it stored its split partial.
+// Returns true (in all threads) in the workgroup that arrived last for its
+// unit; that workgroup then merges.  Each thread waits for its own partial
+// stores to complete before the barrier, so when the arrival count is seen
+// every partial of the unit is visible to device-scope loads.  The last
+// arrival resets the counter, so the counters are zero again at kernel end.
 __device__ __forceinline__ bool arrive_last(unsigned *counter, int nsplit) {
   __shared__ int s_last;
-  __threadfence();  // release: this thread's partial stores reach device scope
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
-    const unsigned prev = atomicAdd(counter, 1u);
+    const unsigned prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int last = prev == (unsigned)(nsplit - 1);
-    if (last) atomicExch(counter, 0u);
+    if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last = last;
   }
   __syncthreads();
-  const bool last = s_last != 0;
-  if (last) __threadfence();  // acquire: see every other split's partial
-  return last;
+  return s_last != 0;
 }
 
 // Log-sum-exp merge of the nsplit partials of heads head0 .. head0+nh-1 of
-// sequence b into out.  Splits are visited in index order (deterministic).
+// sequence b into out (splits in index order: deterministic, and the same
+// arithmetic as the merge kernel).
 template <typename T, int D>
-__device__ void merge_splits(const DecodeParams &p, int b, int head0, int nh, int nsplit) {
+__device__ void merge_heads(const DecodeParams &p, int b, int head0, int nh, int nsplit) {
   for (int idx = threadIdx.x; idx < nh * (D / 4); idx += blockDim.x) {
     const int j = idx / (D / 4), c = (idx % (D / 4)) * 4;
     const size_t hs = ((size_t)b * p.H + head0 + j) * p.S;
+    const float *ml = reinterpret_cast<const float *>(p.ws_ml + hs);
     float M = kNegInf;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, p.ws_ml[hs + s].x);
+    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, load_pair(ml + 2 * s).x);
     const float sh = safe_shift(M);
     float L = 0.f, o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
     for (int s = 0; s < nsplit; ++s) {
-      const float2 ml = p.ws_ml[hs + s];
-      const float a = fast_exp2(ml.x - sh);
-      const float4 o = *reinterpret_cast<const float4 *>(p.ws_o + (hs + s) * D + c);
-      L += ml.y * a;
-      o0 += o.x * a;
-      o1 += o.y * a;
-      o2 += o.z * a;
-      o3 += o.w * a;
+      const float2 h = load_pair(ml + 2 * s);
+      const float a = fast_exp2(h.x - sh);
+      const float2 x = load_pair(p.ws_o + (hs + s) * D + c);
+      const float2 y = load_pair(p.ws_o + (hs + s) * D + c + 2);
+      L += h.y * a;
+      o0 += x.x * a;
+      o1 += x.y * a;
+      o2 += y.x * a;
+      o3 += y.y * a;
     }
     const float inv = 1.f / L;
     Store<T>::four(p.out, ((size_t)b * p.H + head0 + j) * D + c, o0 * inv, o1 * inv, o2 * inv, o3 * inv);
@@ -120,6 +145,7 @@ __device__ void merge_splits(const DecodeParams &p, int b, int head0, int nh, in
 // Host-side launchers (one per kernel translation unit).
 hipError_t launch_decode_valu(const DecodeParams &p, int dtype, int D, int RC, unsigned grid, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeParams &p, int D, int HB, unsigned grid, hipStream_t stream);
+hipError_t launch_merge(const DecodeParams &p, int dtype, int D, int heads_per_unit, hipStream_t stream);
 hipError_t launch_meanpool(const float *w, int d_model, int H, int G, int h, float *w_out, hipStream_t stream);
 hipError_t launch_fill_zero(void *ptr, size_t bytes, hipStream_t stream);
 

@@ -26,12 +26,6 @@ __global__ __launch_bounds__(256) void meanpool_kernel(const float *__restrict__
   w_out[idx] = (float)(acc / (double)r);
 }
 
-__global__ __launch_bounds__(256) void fill_zero_kernel(uint4 *p, size_t n16, unsigned char *tail, size_t ntail) {
-  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n16) p[i] = make_uint4(0u, 0u, 0u, 0u);
-  if (i < ntail) tail[i] = 0;
-}
-
 }  // namespace
 
 hipError_t launch_meanpool(const float *w, int d_model, int H, int G, int h, float *w_out, hipStream_t stream) {
@@ -39,16 +33,6 @@ hipError_t launch_meanpool(const float *w, int d_model, int H, int G, int h, flo
   if (total == 0) return hipSuccess;
   const size_t blocks = (total + 255) / 256;
   hipLaunchKernelGGL(meanpool_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, w, H, G, h, total, w_out);
-  return hipGetLastError();
-}
-
-hipError_t launch_fill_zero(void *ptr, size_t bytes, hipStream_t stream) {
-  const size_t n16 = bytes / 16, ntail = bytes % 16;
-  const size_t n = n16 > ntail ? n16 : ntail;
-  if (n == 0) return hipSuccess;
-  const size_t blocks = (n + 255) / 256;
-  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, static_cast<uint4 *>(ptr), n16,
-                     static_cast<unsigned char *>(ptr) + n16 * 16, ntail);
   return hipGetLastError();
 }
 

@@ -57,17 +57,18 @@ typedef enum {
 
 /*
  * Bytes of device workspace that gqa_decode needs for this shape (0 when it
- * needs none).  The workspace holds per-split partial results and per-(b,g)
- * arrival counters.  Returns 0 for arguments gqa_decode would reject.
+ * needs none).  The workspace holds per-split partial results and, in its
+ * first 256 KiB, arrival counters.  Returns 0 for arguments gqa_decode would
+ * reject.
  */
 size_t gqa_decode_workspace_size(int B, int H, int G, int d, int Lmax, gqa_dtype dtype);
 
 /*
  * Clears a workspace before its first use (enqueues a fill kernel on
- * `stream`).  Equivalent to filling the buffer with zero bytes.  After a
- * completed gqa_decode call the workspace is again in this cleared state, so
- * one workspace serves any number of sequential calls of any shape whose
- * requirement it meets.
+ * `stream`; the same as filling it with zero bytes).  Every completed
+ * gqa_decode call leaves the counter region zero again, so a cleared
+ * workspace serves any number of later calls, of any shape whose size
+ * requirement it meets.  workspace_bytes = 0 is a no-op.
  */
 gqa_status gqa_workspace_init(void *workspace, size_t workspace_bytes, hipStream_t stream);
 
@@ -91,14 +92,34 @@ gqa_status gqa_workspace_init(void *workspace, size_t workspace_bytes, hipStream
  *             once (to nearest even) from binary32 accumulation.
  *   workspace device buffer of workspace_bytes >= gqa_decode_workspace_size
  *             (may be NULL when that size is 0), 256-byte aligned, cleared
- *             once by gqa_workspace_init (or any zero fill) before first use.
+ *             once before first use (gqa_workspace_init or any zero fill),
+ *             and owned by this call until the work completes on `stream`.
  *   stream    HIP stream the work is enqueued on (NULL: the null stream).
  *
+ * Enqueues one kernel: a workgroup per (sequence, K/V head, context split)
+ * streams that part of the cache once for all query heads of the group; when
+ * a sequence spans several splits, the workgroup that finishes its (sequence,
+ * K/V head) last merges the split results (log-sum-exp) into out.  Above
+ * 65536 (sequence, K/V head) units, or with the environment variable
+ * GQA_MERGE=kernel, a second kernel does that merge instead.
  * NaN or Inf inside the attended positions propagate to the output.
  */
 gqa_status gqa_decode(const void *q, const void *k_cache, const void *v_cache, const int32_t *seq_lens,
                       int B, int H, int G, int d, int Lmax, float scale, gqa_dtype dtype, void *out,
                       void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * gqa_decode in two phases, for callers that schedule or time them apart:
+ * phase 1 enqueues the split kernel (which completes out by itself unless the
+ * merge runs as a separate kernel), phase 2 only that separate merge kernel
+ * (nothing when it is not needed), phase 0 both - exactly gqa_decode.  Phase 2
+ * must follow phase 1 of the same arguments on the same stream with the
+ * workspace untouched in between.  Other arguments and status codes as for
+ * gqa_decode; an unknown phase gives GQA_ERR_UNSUPPORTED.
+ */
+gqa_status gqa_decode_phase(int phase, const void *q, const void *k_cache, const void *v_cache,
+                            const int32_t *seq_lens, int B, int H, int G, int d, int Lmax, float scale,
+                            gqa_dtype dtype, void *out, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * The pages' checkpoint conversion step, numeric core only: wikillm

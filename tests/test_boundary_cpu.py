@@ -98,9 +98,9 @@ def test_workspace_size_model(lib, monkeypatch):
     monkeypatch.setenv("GQA_CHUNK", "128")
     S = 4
     need = lib.gqa_decode_workspace_size(B, H, G, d, L, BF16)
-    # partial outputs + (max, sum) pairs + counters, each region 256-byte aligned
-    assert need >= B * H * S * d * 4 + B * H * S * 8 + B * G * 4
-    assert need <= B * H * S * d * 4 + B * H * S * 8 + B * G * 4 + 2 * 256
+    # 256 KiB of arrival counters, (max, sum) pairs, then partial outputs
+    ml = (B * H * S * 8 + 255) // 256 * 256
+    assert need == 256 * 1024 + ml + B * H * S * d * 4
     monkeypatch.setenv("GQA_CHUNK", str(L))
     assert lib.gqa_decode_workspace_size(B, H, G, d, L, BF16) == 0  # one split: no workspace
     assert lib.gqa_decode_workspace_size(B, 6, 4, d, L, BF16) == 0  # rejected shape
@@ -130,6 +130,14 @@ def test_meanpool_argument_errors(lib):
 def test_workspace_init_arguments(lib):
     assert lib.gqa_workspace_init(None, 0, None) == OK
     assert lib.gqa_workspace_init(None, 64, None) == NULL
+
+
+def test_phase_argument(lib):
+    args = (P, P, P, P, 2, 8, 2, 128, 512, 0.125, BF16, P, P, 1 << 30, None)
+    assert lib.gqa_decode_phase(3, *args) == UNSUP
+    assert lib.gqa_decode_phase(-1, *args) == UNSUP
+    assert lib.gqa_decode_phase(1, P, P, P, P, 2, 6, 4, 128, 512, 0.125, BF16, P, P, 0, None) == SHAPE
+    assert lib.gqa_decode_phase(2, None, None, None, None, 0, 8, 2, 128, 512, 0.125, BF16, None, None, 0, None) == OK
 
 
 def test_binding_rejects_bad_tensors():

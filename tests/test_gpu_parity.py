@@ -39,7 +39,7 @@ def env(monkeypatch):
                 monkeypatch.delenv(k, raising=False)
             else:
                 monkeypatch.setenv(k, str(v))
-    set_(GQA_KERNEL=None, GQA_CHUNK=None, GQA_TARGET_WGS=None, GQA_MAX_CHUNK=None)
+    set_(GQA_KERNEL=None, GQA_CHUNK=None, GQA_TARGET_WGS=None, GQA_MAX_CHUNK=None, GQA_MERGE=None)
     return set_
 
 
@@ -99,9 +99,11 @@ SMALL = [
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("kernel", ["default", "valu"])
 @pytest.mark.parametrize("chunk", [None, 128, 100000])
-def test_small_parity(env, case, dtype, kernel, chunk):
+@pytest.mark.parametrize("merge", ["fused", "kernel"])
+def test_small_parity(env, case, dtype, kernel, chunk, merge):
     B, H, G, d, L, lens = case
-    env(GQA_KERNEL=None if kernel == "default" else kernel, GQA_CHUNK=chunk)
+    env(GQA_KERNEL=None if kernel == "default" else kernel, GQA_CHUNK=chunk,
+        GQA_MERGE=None if merge == "fused" else "kernel")
     q, k, v, lens_t, scale = rand_case(B, H, G, d, L, lens, dtype, seed=sum(case[:5]) + 7 * len(lens))
     out = run_gpu(q, k, v, lens_t, scale)
     check(out, oracle_out(q, k, v, lens_t, scale), dtype, "%s %s chunk=%s %s" % (dtype, kernel, chunk, case))
@@ -204,6 +206,28 @@ def test_outlier_rows_alternative_reading(env):
     k[rows] = (k[rows].float() * 20).to(k.dtype)
     out = run_gpu(q, k, v, lens, scale)
     check(out, oracle_out(q, k, v, lens, scale), "bf16", "outlier rows")
+
+
+@pytest.mark.parametrize("kernel", ["default", "valu"])
+def test_fused_merge_matches_merge_kernel(env, kernel):
+    """The in-kernel merge (last-arriving workgroup) and the separate merge
+    kernel do the same arithmetic in the same order: results are bit-equal,
+    call after call, on shapes with many concurrent splits."""
+    cases = [rand_case(16, 32, 8, 128, 4096, [4096] * 16, "bf16", seed=21),
+             rand_case(32, 64, 8, 64, 2048, [2048 - 37 * i for i in range(32)], "bf16", seed=22),
+             rand_case(4, 16, 4, 128, 3000, [3000, 1, 1500, 2999], "f32", seed=23)]
+    for q, k, v, lens, scale in cases:
+        env(GQA_KERNEL=None if kernel == "default" else kernel, GQA_CHUNK=256, GQA_MERGE="kernel")
+        ref = run_gpu(q, k, v, lens, scale).clone()
+        env(GQA_MERGE=None)
+        for _ in range(30):
+            out = gqa.decode(q, k, v, lens, scale)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref)
+        outs = [gqa.decode(q, k, v, lens, scale).clone() for _ in range(20)]
+        torch.cuda.synchronize()
+        for o in outs:
+            assert torch.equal(o, ref)
 
 
 # --------------------------------------------------------------- the named workloads at full size
