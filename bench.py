@@ -85,7 +85,7 @@ def cpu_baseline(w, q, k, v, lens, out_gpu, budget_s: float):
         reps += 1
         if ref is None:
             ref = np.stack(outs)
-        if elapsed >= budget_s or reps >= 20:
+        if elapsed >= budget_s or reps >= 1000:
             break
     got = out_gpu.float().cpu().double().numpy()
     err = float(np.max(np.abs(got - ref)))
@@ -195,6 +195,37 @@ def calibrate_copy(args):
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "calls": args.steps}), flush=True)
 
 
+def counter_mean(d, counter, kernel_substr):
+    """Mean per-dispatch value of a rocprofv3 --pmc counter for kernels whose name contains kernel_substr."""
+    vals = [float(r["Counter_Value"]) for r in _read_csvs(d, "counter_collection.csv")
+            if r.get("Counter_Name") == counter and kernel_substr in r.get("Kernel_Name", "")]
+    if not vals:
+        raise SystemExit("no %s samples for %s in %s" % (counter, kernel_substr, d))
+    return sum(vals) / len(vals), len(vals)
+
+
+def write_traffic(args):
+    """HBM bytes per dispatch of the decode kernel from FETCH_SIZE / WRITE_SIZE
+    passes (KiB per dispatch), each scaled by what the same counter reads for a
+    plain 1 GiB device copy; written to profiles/traffic_<workload>.json."""
+    fetch, nf = counter_mean(args.fetch_dir, "FETCH_SIZE", "decode_")
+    write, nw = counter_mean(args.write_dir, "WRITE_SIZE", "decode_")
+    cf, _ = counter_mean(args.copy_fetch_dir, "FETCH_SIZE", "copyBuffer")
+    cw, _ = counter_mean(args.copy_write_dir, "WRITE_SIZE", "copyBuffer")
+    copy_kib = (1 << 30) / 1024.0
+    f_fac, w_fac = cf / copy_kib, cw / copy_kib
+    rec = {
+        "workload": args.workload, "source_hash": kernel_source_hash(),
+        "fetch_kib_per_dispatch": fetch, "write_kib_per_dispatch": write, "dispatches": [nf, nw],
+        "copy_fetch_factor": f_fac, "copy_write_factor": w_fac,
+        "bytes_per_dispatch": (fetch / f_fac + write / w_fac) * 1024.0,
+    }
+    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % args.workload)
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
 def _read_csvs(d, suffix):
     rows = []
     for f in sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True)):
@@ -236,9 +267,18 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time to aim for")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--summarize-rocprof", metavar="DIR")
+    ap.add_argument("--write-traffic", action="store_true",
+                    help="combine counter runs (--fetch-dir, --write-dir, --copy-fetch-dir, --copy-write-dir)")
+    ap.add_argument("--fetch-dir")
+    ap.add_argument("--write-dir")
+    ap.add_argument("--copy-fetch-dir")
+    ap.add_argument("--copy-write-dir")
     args = ap.parse_args()
     if args.summarize_rocprof:
         print(summarize_rocprof(args.summarize_rocprof))
+        return 0
+    if args.write_traffic:
+        write_traffic(args)
         return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -61,18 +61,24 @@ gqa_status check_shape(int B, int H, int G, int d, int Lmax, gqa_dtype dt) {
   return GQA_OK;
 }
 
-// Decode launch plan.  One workgroup per (b, g, head chunk, split); splits
-// are sized so that the grid holds about GQA_TARGET_WGS workgroups (default
-// 2048, eight per compute unit) with at most GQA_MAX_CHUNK positions each.
-// When a sequence spans several splits, the workgroup that finishes its
-// (b, g) unit last merges the partials inside the same kernel; with more
-// units than counters (or GQA_MERGE=kernel) a second kernel merges instead.
+// Decode launch plan (tuned on MI355X with the workload sweep):
+//  - kernel: bfloat16 uses the matrix-core kernel for r = H/G in 2..64 and
+//    the VALU kernel for r = 1, where it measured faster (no 16-head padding);
+//    fp32 always uses the VALU kernel.  GQA_KERNEL=valu|mfma overrides.
+//  - splits: one workgroup per (b, g, head chunk, split).  The split length
+//    is chosen so that the grid holds about GQA_TARGET_WGS workgroups (default
+//    256 for d = 128, 512 for d = 64: one or two per compute unit), clamped to
+//    [512, GQA_MAX_CHUNK = 4096] positions: long splits amortise each
+//    workgroup's prologue and epilogue, the cap keeps ragged batches balanced.
+//  - when a sequence spans several splits, the workgroup that finishes its
+//    (b, g) unit last merges the partials inside the same kernel; with more
+//    units than counters (or GQA_MERGE=kernel) a second kernel merges instead.
 gqa_status make_plan(int B, int H, int G, int d, int Lmax, gqa_dtype dt, Plan *pl) {
   const int r = H / G;
   const char *force = getenv("GQA_KERNEL");
-  int kind = dt == GQA_BF16 ? KIND_MFMA : KIND_VALU;
+  int kind = (dt == GQA_BF16 && r >= 2 && r <= 64) ? KIND_MFMA : KIND_VALU;
   if (force && strcmp(force, "valu") == 0) kind = KIND_VALU;
-  if (kind == KIND_MFMA && r > 64) kind = KIND_VALU;
+  if (force && strcmp(force, "mfma") == 0 && dt == GQA_BF16 && r <= 64) kind = KIND_MFMA;
   pl->kind = kind;
   if (kind == KIND_MFMA) {
     const int hb = (r + 15) / 16;
@@ -85,14 +91,15 @@ gqa_status make_plan(int B, int H, int G, int d, int Lmax, gqa_dtype dt, Plan *p
     pl->HB = 0;
   }
   const long units = (long)B * G * pl->HC;
-  const int target = env_int("GQA_TARGET_WGS", 2048);
-  const int max_chunk = env_int("GQA_MAX_CHUNK", 2048);
+  const int target = env_int("GQA_TARGET_WGS", d == 64 ? 512 : 256);
+  const int max_chunk = env_int("GQA_MAX_CHUNK", 4096);
   int chunk = env_int("GQA_CHUNK", 0);
   if (chunk == 0) {
     long S = (target + units - 1) / units;
     if (S < 1) S = 1;
-    chunk = (int)round_up((size_t)ceil_div(Lmax, S), 128);
-    if (chunk > max_chunk) chunk = (int)round_up((size_t)max_chunk, 128);
+    chunk = (int)round_up((size_t)ceil_div(Lmax, S), 32);
+    if (chunk < 512) chunk = 512;
+    if (chunk > max_chunk) chunk = max_chunk;
   }
   if (chunk > Lmax) chunk = Lmax;
   pl->chunk = chunk;

@@ -85,11 +85,14 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeParams p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane >> 4, nn = lane & 15;
 
-  unsigned id = blockIdx.x;
-  const int s = id % p.S;
-  id /= p.S;
-  const int g = id % p.G;
-  const int b = id / p.G;
+  // Split index slowest: consecutive workgroups (which the dispatcher deals
+  // round-robin to the XCDs) are different (b, g) units of one split, so
+  // every XCD gets an even share of the units whatever their lengths.
+  const unsigned units = (unsigned)p.B * p.G;
+  const int s = blockIdx.x / units;
+  const unsigned u = blockIdx.x % units;
+  const int g = u % p.G;
+  const int b = u / p.G;
 
   const int n = clamp_len(p, b);
   const int nsplit = num_splits(n, p.chunk);

@@ -62,9 +62,10 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeParams p) {
   const int sub = lane % LPR;
   const int rg = wave * RPW + lane / LPR;
 
-  unsigned id = blockIdx.x;
-  const int s = id % p.S;
-  id /= p.S;
+  // Split index slowest (see the MFMA kernel): units spread over the XCDs.
+  const unsigned units = (unsigned)p.B * p.G * p.HC;
+  const int s = blockIdx.x / units;
+  unsigned id = blockIdx.x % units;
   const int hc = id % p.HC;
   id /= p.HC;
   const int g = id % p.G;

@@ -114,28 +114,42 @@ __device__ __forceinline__ bool arrive_last(unsigned *counter, int nsplit) {
 }
 
 // Log-sum-exp merge of the nsplit partials of heads head0 .. head0+nh-1 of
-// sequence b into out (splits in index order: deterministic, and the same
-// arithmetic as the merge kernel).
+// sequence b into out.  Splits are taken in index order, eight at a time: the
+// loads of a batch are issued together, then folded into a running
+// (max, weight sum, output) with rescaling when the max grows.  Deterministic;
+// the separate merge kernel calls this same routine.
 template <typename T, int D>
 __device__ void merge_heads(const DecodeParams &p, int b, int head0, int nh, int nsplit) {
+  constexpr int kBatch = 8;
   for (int idx = threadIdx.x; idx < nh * (D / 4); idx += blockDim.x) {
     const int j = idx / (D / 4), c = (idx % (D / 4)) * 4;
     const size_t hs = ((size_t)b * p.H + head0 + j) * p.S;
     const float *ml = reinterpret_cast<const float *>(p.ws_ml + hs);
-    float M = kNegInf;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, load_pair(ml + 2 * s).x);
-    const float sh = safe_shift(M);
-    float L = 0.f, o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-      const float2 h = load_pair(ml + 2 * s);
-      const float a = fast_exp2(h.x - sh);
-      const float2 x = load_pair(p.ws_o + (hs + s) * D + c);
-      const float2 y = load_pair(p.ws_o + (hs + s) * D + c + 2);
-      L += h.y * a;
-      o0 += x.x * a;
-      o1 += x.y * a;
-      o2 += y.x * a;
-      o3 += y.y * a;
+    float M = kNegInf, L = 0.f, o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+    for (int s0 = 0; s0 < nsplit; s0 += kBatch) {
+      float2 h[kBatch], x[kBatch], y[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        if (s0 + i < nsplit) {
+          h[i] = load_pair(ml + 2 * (s0 + i));
+          x[i] = load_pair(p.ws_o + (hs + s0 + i) * D + c);
+          y[i] = load_pair(p.ws_o + (hs + s0 + i) * D + c + 2);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        if (s0 + i < nsplit) {
+          const float mn = fmaxf(M, h[i].x);
+          const float sh = safe_shift(mn);
+          const float a_old = fast_exp2(M - sh), a = fast_exp2(h[i].x - sh);
+          M = mn;
+          L = L * a_old + h[i].y * a;
+          o0 = o0 * a_old + x[i].x * a;
+          o1 = o1 * a_old + x[i].y * a;
+          o2 = o2 * a_old + y[i].x * a;
+          o3 = o3 * a_old + y[i].y * a;
+        }
+      }
     }
     const float inv = 1.f / L;
     Store<T>::four(p.out, ((size_t)b * p.H + head0 + j) * D + c, o0 * inv, o1 * inv, o2 * inv, o3 * inv);

@@ -111,9 +111,13 @@ def test_kernel_selection(lib, monkeypatch):
     assert lib.gqa_decode_kernel_kind(16, 32, 8, 128, 4096, BF16) == 1
     assert lib.gqa_decode_kernel_kind(1, 8, 2, 64, 256, F32) == 0
     assert lib.gqa_decode_kernel_kind(1, 128, 1, 64, 256, BF16) == 0  # more than 64 heads per group
+    assert lib.gqa_decode_kernel_kind(32, 64, 64, 64, 2048, BF16) == 0  # r = 1: VALU measured faster
     assert lib.gqa_decode_kernel_kind(1, 6, 4, 64, 256, BF16) == -1
     monkeypatch.setenv("GQA_KERNEL", "valu")
     assert lib.gqa_decode_kernel_kind(16, 32, 8, 128, 4096, BF16) == 0
+    monkeypatch.setenv("GQA_KERNEL", "mfma")
+    assert lib.gqa_decode_kernel_kind(32, 64, 64, 64, 2048, BF16) == 1
+    assert lib.gqa_decode_kernel_kind(1, 8, 2, 64, 256, F32) == 0  # no fp32 matrix-core path
 
 
 def test_meanpool_argument_errors(lib):
