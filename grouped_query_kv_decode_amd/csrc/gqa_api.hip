@@ -49,6 +49,7 @@ constexpr long kMaxFusedUnits = kCounterBytes / sizeof(unsigned);
 struct Plan {
   int kind;
   int chunk, S, HC, RC, HB;
+  int NW;  // waves per workgroup (matrix-core kernel)
   int fused;
   unsigned grid;
   size_t ml_off, o_off, ws_bytes;
@@ -65,11 +66,15 @@ gqa_status check_shape(int B, int H, int G, int d, int Lmax, gqa_dtype dt) {
 //  - kernel: bfloat16 uses the matrix-core kernel for r = H/G in 2..64 and
 //    the VALU kernel for r = 1, where it measured faster (no 16-head padding);
 //    fp32 always uses the VALU kernel.  GQA_KERNEL=valu|mfma overrides.
+//  - workgroups of the matrix-core kernel have 8 waves for d = 64 or splits
+//    longer than 2048 positions, else 4 (GQA_WAVES = 4, 8 or 16 overrides),
+//    capped by the register budget for the group's head blocks.
 //  - splits: one workgroup per (b, g, head chunk, split).  The split length
-//    is chosen so that the grid holds about GQA_TARGET_WGS workgroups (default
-//    256 for d = 128, 512 for d = 64: one or two per compute unit), clamped to
-//    [512, GQA_MAX_CHUNK = 4096] positions: long splits amortise each
-//    workgroup's prologue and epilogue, the cap keeps ragged batches balanced.
+//    is chosen so that the grid holds about GQA_TARGET_WGS = 256 workgroups
+//    (one per compute unit), clamped to [512, GQA_MAX_CHUNK = 4096]
+//    positions: long splits amortise each workgroup's prologue and epilogue,
+//    the cap keeps ragged batches balanced.  Half the compute units cannot
+//    keep HBM busy, so a shape with fewer (b, g) units than that is split.
 //  - when a sequence spans several splits, the workgroup that finishes its
 //    (b, g) unit last merges the partials inside the same kernel; with more
 //    units than counters (or GQA_MERGE=kernel) a second kernel merges instead.
@@ -80,9 +85,11 @@ gqa_status make_plan(int B, int H, int G, int d, int Lmax, gqa_dtype dt, Plan *p
   if (force && strcmp(force, "valu") == 0) kind = KIND_VALU;
   if (force && strcmp(force, "mfma") == 0 && dt == GQA_BF16 && r <= 64) kind = KIND_MFMA;
   pl->kind = kind;
+  pl->NW = 4;
   if (kind == KIND_MFMA) {
     const int hb = (r + 15) / 16;
     pl->HB = hb <= 1 ? 1 : (hb <= 2 ? 2 : 4);
+    pl->NW = 4;  // chosen below, once the split length is known
     pl->RC = 0;
     pl->HC = 1;
   } else {
@@ -91,7 +98,7 @@ gqa_status make_plan(int B, int H, int G, int d, int Lmax, gqa_dtype dt, Plan *p
     pl->HB = 0;
   }
   const long units = (long)B * G * pl->HC;
-  const int target = env_int("GQA_TARGET_WGS", d == 64 ? 512 : 256);
+  const int target = env_int("GQA_TARGET_WGS", 256);
   const int max_chunk = env_int("GQA_MAX_CHUNK", 4096);
   int chunk = env_int("GQA_CHUNK", 0);
   if (chunk == 0) {
@@ -103,6 +110,15 @@ gqa_status make_plan(int B, int H, int G, int d, int Lmax, gqa_dtype dt, Plan *p
   }
   if (chunk > Lmax) chunk = Lmax;
   pl->chunk = chunk;
+  if (kind == KIND_MFMA) {
+    // 8 waves for d = 64 and for splits longer than 2048 positions (measured
+    // faster there), 4 otherwise; only where the head blocks fit the
+    // register budget of the larger workgroup.
+    const int nw_max = (pl->HB == 1 && d == 64) ? 16 : (pl->HB <= 2 ? 8 : 4);
+    const int nw_def = (d == 64 || chunk > 2048) ? 8 : 4;
+    const int nw = env_int("GQA_WAVES", nw_def);
+    pl->NW = (nw == 8 || nw == 16) && nw <= nw_max ? nw : 4;
+  }
   pl->S = ceil_div(Lmax, chunk);
   const unsigned long long grid = (unsigned long long)units * pl->S;
   if (grid == 0 || grid > 0x7fffffffULL) return GQA_ERR_SIZE;
@@ -178,6 +194,7 @@ gqa_status gqa_decode_phase(int phase, const void *q, const void *k_cache, const
   p.ws_ml = pl.ws_bytes ? reinterpret_cast<float2 *>(ws + pl.ml_off) : nullptr;
   p.ws_o = pl.ws_bytes ? reinterpret_cast<float *>(ws + pl.o_off) : nullptr;
   p.fused = pl.fused;
+  p.contig = env_int("GQA_CONTIG", 0) == 1;
   p.B = B;
   p.H = H;
   p.G = G;
@@ -189,7 +206,7 @@ gqa_status gqa_decode_phase(int phase, const void *q, const void *k_cache, const
   p.scale_log2 = (float)sl2;
 
   if (phase != 2) {
-    const hipError_t e = pl.kind == KIND_MFMA ? gqa::launch_decode_mfma(p, d, pl.HB, pl.grid, stream)
+    const hipError_t e = pl.kind == KIND_MFMA ? gqa::launch_decode_mfma(p, d, pl.HB, pl.NW, pl.grid, stream)
                                               : gqa::launch_decode_valu(p, (int)dtype, d, pl.RC, pl.grid, stream);
     if (e != hipSuccess) return hip_fail(e);
   }

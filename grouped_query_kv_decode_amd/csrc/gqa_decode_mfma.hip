@@ -75,9 +75,10 @@ __device__ __forceinline__ void pv_steps(f32x4 (&o)[HB][DB], const Row *vR, cons
   }
 }
 
-template <int D, int HB>
-__global__ __launch_bounds__(256) void decode_mfma(DecodeParams p) {
+template <int D, int HB, int NW, int TPI>
+__global__ __launch_bounds__(64 * NW) void decode_mfma(DecodeParams p) {
   static_assert(D == 64 || D == 128, "head dim");
+  static_assert(TPI == 1 || TPI == 2, "tiles per iteration");
   constexpr int KB = D / 32;  // QK MFMAs per 16-position half
   constexpr int DB = D / 16;  // PV MFMAs (dimension blocks)
   typedef typename std::conditional<D == 128, u32x4, u32x2>::type VRow;
@@ -94,15 +95,8 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeParams p) {
   const int g = u % p.G;
   const int b = u / p.G;
 
-  const int n = clamp_len(p, b);
-  const int nsplit = num_splits(n, p.chunk);
-  if (s >= nsplit) return;
   const int head0 = g * p.r;
-  if (n == 0) {
-    write_zero_heads<__bf16, D>(p, b, head0, p.r);
-    return;
-  }
-  const int t0 = s * p.chunk, t1 = min(t0 + p.chunk, n);
+  const int t0 = s * p.chunk;
 
   // B operand of the score MFMAs: q of head hb*16 + nn, dims kb*32 + 8c .. +7.
   u32x4 qB[HB][KB];
@@ -124,16 +118,6 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeParams p) {
   const int koff = (8 * (nn >> 2) + (nn & 3)) * D + 8 * c;
   const int voff = 8 * c * D + VPL * nn;
 
-  f32x4 o[HB][DB];
-  float m[HB], l[HB];
-#pragma unroll
-  for (int hb = 0; hb < HB; ++hb) {
-    m[hb] = kNegInf;
-    l[hb] = 0.f;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) o[hb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
   // One 32-position tile: K rows for the two score halves, V rows 8c .. 8c+7.
   struct Tile {
     u32x4 kA[2][KB];
@@ -151,6 +135,37 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeParams p) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) T.vR[u] = *reinterpret_cast<const VRow *>(vt + voff + u * D);
   };
+
+  // The wave's first tile is requested before the sequence length arrives
+  // (q, that tile and the length then share one memory latency).  Its rows
+  // lie inside the cache slab; they are used only if the whole tile turns
+  // out to be inside the split, otherwise the tile is loaded again below.
+  // Limited to the leading splits, so workgroups of splits past a short
+  // sequence's end waste little.
+  const int t_first = t0 + 32 * wave;
+  const bool spec = !p.contig && (s == 0 || p.S <= 2) && t_first + 32 <= min(t0 + p.chunk, p.Lmax);
+  Tile T_first;
+  if (spec) load_full(T_first, t_first);
+
+  const int n = clamp_len(p, b);
+  const int nsplit = num_splits(n, p.chunk);
+  if (s >= nsplit) return;
+  if (n == 0) {
+    write_zero_heads<__bf16, D>(p, b, head0, p.r);
+    return;
+  }
+  const int t1 = min(t0 + p.chunk, n);
+
+  f32x4 o[HB][DB];
+  float m[HB], l[HB];
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) {
+    m[hb] = kNegInf;
+    l[hb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[hb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
   // The last tile of a split: rows past the split end are clamped to its last
   // row (never past the sequence length) and masked out of the softmax.
   auto load_tail = [&](Tile &T, int tt) {
@@ -217,13 +232,40 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeParams p) {
     pv_steps<0, DB, HB>(o, T.vR, pB);
   };
 
-  // Each wave takes every fourth 32-position tile of the split.
-  for (int tt = t0 + 32 * wave; tt < t1; tt += 128) {
+  // Tiles of the split go to the waves either interleaved (wave w takes
+  // every NW-th 32-position tile) or as contiguous runs (p.contig), TPI tiles
+  // per iteration (their loads are issued together).
+  int tt, te, kStride;
+  if (p.contig) {
+    const int ntiles = (t1 - t0 + 31) / 32;
+    const int per = (ntiles + NW - 1) / NW;
+    tt = t0 + 32 * per * wave;
+    te = min(t1, tt + 32 * per);
+    kStride = 32;
+  } else {
+    tt = t0 + 32 * wave;
+    te = t1;
+    kStride = 32 * NW;
+    if (spec && tt + 32 <= t1) {  // the prefetched first tile is whole: use it
+      compute(T_first, tt, false);
+      tt += kStride;
+    }
+  }
+  if (TPI == 2) {
+    for (; tt + kStride + 32 <= te; tt += 2 * kStride) {
+      Tile T0, T1;
+      load_full(T0, tt);
+      load_full(T1, tt + kStride);
+      compute(T0, tt, false);
+      compute(T1, tt + kStride, false);
+    }
+  }
+  for (; tt < te; tt += kStride) {
     Tile T;
     if (tt + 32 <= t1) {
       load_full(T, tt);
       compute(T, tt, false);
-    } else {
+    } else {  // only the split's last tile can be partial
       load_tail(T, tt);
       compute(T, tt, true);
     }
@@ -233,11 +275,15 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeParams p) {
 #pragma unroll
   for (int hb = 0; hb < HB; ++hb) l[hb] = group_sum(l[hb]);
 
-  // Merge the four waves through LDS, in wave order (deterministic).
+  // Merge the NW waves through LDS, in wave order (deterministic).  When the
+  // per-wave outputs fit in 64 KiB each wave stores its own and one barrier
+  // suffices; otherwise the waves add into one buffer in turn.
   constexpr int NHB = 16 * HB;
   constexpr int LD = D + 4;
-  __shared__ float sm_m[4][NHB], sm_l[4][NHB];
-  __shared__ float sm_o[NHB * LD];
+  constexpr bool kParallel = NW * NHB * LD * 4 <= 64 * 1024;
+  constexpr int kRegions = kParallel ? NW : 1;
+  __shared__ float sm_m[NW][NHB], sm_l[NW][NHB];
+  __shared__ float sm_o[kRegions * NHB * LD];
   if (c == 0) {
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
@@ -245,48 +291,80 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeParams p) {
       sm_l[wave][hb * 16 + nn] = l[hb];
     }
   }
-  __syncthreads();
-  float a_self[HB];
+  // output row m = 4c + i of PV MFMA db holds dimension VPL*m + db
+  if (kParallel) {
 #pragma unroll
-  for (int hb = 0; hb < HB; ++hb) {
-    const int j = hb * 16 + nn;
-    const float M = fmaxf(fmaxf(sm_m[0][j], sm_m[1][j]), fmaxf(sm_m[2][j], sm_m[3][j]));
-    a_self[hb] = fast_exp2(m[hb] - safe_shift(M));
-  }
-  for (int w = 0; w < 4; ++w) {
-    if (wave == w) {
+    for (int hb = 0; hb < HB; ++hb) {
+      float *row = sm_o + (wave * NHB + hb * 16 + nn) * LD;
 #pragma unroll
-      for (int hb = 0; hb < HB; ++hb) {
-        float *row = sm_o + (hb * 16 + nn) * LD;
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            // output row m = 4c + i of MFMA db holds dimension dpm*m + db
-            const int dim = (D == 128 ? 8 : 4) * (4 * c + i) + db;
-            const float add = o[hb][db][i] * a_self[hb];
-            row[dim] = w == 0 ? add : row[dim] + add;
-          }
-      }
+        for (int db = 0; db < DB; ++db) row[VPL * (4 * c + i) + db] = o[hb][db][i];
     }
     __syncthreads();
+  } else {
+    __syncthreads();
+    float a_self[HB];
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+      const int j = hb * 16 + nn;
+      float M = sm_m[0][j];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) M = fmaxf(M, sm_m[w][j]);
+      a_self[hb] = fast_exp2(m[hb] - safe_shift(M));
+    }
+    for (int w = 0; w < NW; ++w) {
+      if (wave == w) {
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) {
+          float *row = sm_o + (hb * 16 + nn) * LD;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+              const int dim = VPL * (4 * c + i) + db;
+              const float add = o[hb][db][i] * a_self[hb];
+              row[dim] = w == 0 ? add : row[dim] + add;
+            }
+        }
+      }
+      __syncthreads();
+    }
   }
 
   for (int idx = threadIdx.x; idx < p.r * (D / 4); idx += blockDim.x) {
     const int j = idx / (D / 4), cc = (idx % (D / 4)) * 4;
-    const float M = fmaxf(fmaxf(sm_m[0][j], sm_m[1][j]), fmaxf(sm_m[2][j], sm_m[3][j]));
-    const float shj = safe_shift(M);
-    float L = 0.f;
+    float M = sm_m[0][j];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) L += sm_l[w][j] * fast_exp2(sm_m[w][j] - shj);
-    const float *row = sm_o + j * LD + cc;
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, sm_m[w][j]);
+    const float shj = safe_shift(M);
+    float L = 0.f, r0 = 0.f, r1 = 0.f, r2 = 0.f, r3 = 0.f;
+    if (kParallel) {
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float a = fast_exp2(sm_m[w][j] - shj);
+        const float *row = sm_o + (w * NHB + j) * LD + cc;
+        L += sm_l[w][j] * a;
+        r0 += row[0] * a;
+        r1 += row[1] * a;
+        r2 += row[2] * a;
+        r3 += row[3] * a;
+      }
+    } else {
+#pragma unroll
+      for (int w = 0; w < NW; ++w) L += sm_l[w][j] * fast_exp2(sm_m[w][j] - shj);
+      const float *row = sm_o + j * LD + cc;
+      r0 = row[0];
+      r1 = row[1];
+      r2 = row[2];
+      r3 = row[3];
+    }
     if (nsplit == 1) {
       const float inv = 1.f / L;
-      Store<__bf16>::four(p.out, ((size_t)b * p.H + head0 + j) * D + cc, row[0] * inv, row[1] * inv, row[2] * inv,
-                          row[3] * inv);
+      Store<__bf16>::four(p.out, ((size_t)b * p.H + head0 + j) * D + cc, r0 * inv, r1 * inv, r2 * inv, r3 * inv);
     } else {
       const size_t hs = ((size_t)b * p.H + head0 + j) * p.S + s;
-      store_partial4(p.ws_o + hs * D + cc, row[0], row[1], row[2], row[3]);
+      store_partial4(p.ws_o + hs * D + cc, r0, r1, r2, r3);
       if (cc == 0) store_ml(p.ws_ml + hs, M, L);
     }
   }
@@ -295,26 +373,41 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeParams p) {
   merge_heads<__bf16, D>(p, b, head0, p.r, nsplit);
 }
 
-template <int D, int HB>
+template <int D, int HB, int NW>
 hipError_t launch_t(const DecodeParams &p, unsigned grid, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_mfma<D, HB>), dim3(grid), dim3(256), 0, stream, p);
+  // d = 64 tiles are half as long: two per iteration keep as many bytes in flight
+  constexpr int TPI = D == 64 ? 2 : 1;
+  hipLaunchKernelGGL((decode_mfma<D, HB, NW, TPI>), dim3(grid), dim3(64 * NW), 0, stream, p);
   return hipGetLastError();
 }
 
+// Larger workgroups only where the register budget (64 KiB per SIMD split
+// over more waves) holds the head blocks without spilling.
+template <int D, int HB>
+hipError_t launch_nw(const DecodeParams &p, int NW, unsigned grid, hipStream_t stream) {
+  if constexpr (HB == 1 && D == 64) {
+    if (NW == 16) return launch_t<D, HB, 16>(p, grid, stream);
+  }
+  if constexpr (HB <= 2) {
+    if (NW == 8) return launch_t<D, HB, 8>(p, grid, stream);
+  }
+  return launch_t<D, HB, 4>(p, grid, stream);
+}
+
 template <int D>
-hipError_t launch_hb(const DecodeParams &p, int HB, unsigned grid, hipStream_t stream) {
+hipError_t launch_hb(const DecodeParams &p, int HB, int NW, unsigned grid, hipStream_t stream) {
   switch (HB) {
-    case 1: return launch_t<D, 1>(p, grid, stream);
-    case 2: return launch_t<D, 2>(p, grid, stream);
-    case 4: return launch_t<D, 4>(p, grid, stream);
+    case 1: return launch_nw<D, 1>(p, NW, grid, stream);
+    case 2: return launch_nw<D, 2>(p, NW, grid, stream);
+    case 4: return launch_nw<D, 4>(p, NW, grid, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-hipError_t launch_decode_mfma(const DecodeParams &p, int D, int HB, unsigned grid, hipStream_t stream) {
-  return D == 64 ? launch_hb<64>(p, HB, grid, stream) : launch_hb<128>(p, HB, grid, stream);
+hipError_t launch_decode_mfma(const DecodeParams &p, int D, int HB, int NW, unsigned grid, hipStream_t stream) {
+  return D == 64 ? launch_hb<64>(p, HB, NW, grid, stream) : launch_hb<128>(p, HB, NW, grid, stream);
 }
 
 }  // namespace gqa

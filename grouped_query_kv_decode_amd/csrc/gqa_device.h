@@ -24,6 +24,7 @@ struct DecodeParams {
   float2 *ws_ml;           // [B, H, S]     (running max in log2 units, sum of weights)
   unsigned *ws_cnt;        // arrival counter per unit; zero between calls
   int fused;               // 1: the last split of a unit merges; 0: a merge kernel follows
+  int contig;              // matrix-core kernel: contiguous per-wave tile runs instead of interleaved tiles
   int B, H, G, Lmax;
   int r;                   // query heads per K/V head, H / G
   int S;                   // splits per (b, g) in the grid
@@ -158,7 +159,7 @@ __device__ void merge_heads(const DecodeParams &p, int b, int head0, int nh, int
 
 // Host-side launchers (one per kernel translation unit).
 hipError_t launch_decode_valu(const DecodeParams &p, int dtype, int D, int RC, unsigned grid, hipStream_t stream);
-hipError_t launch_decode_mfma(const DecodeParams &p, int D, int HB, unsigned grid, hipStream_t stream);
+hipError_t launch_decode_mfma(const DecodeParams &p, int D, int HB, int NW, unsigned grid, hipStream_t stream);
 hipError_t launch_merge(const DecodeParams &p, int dtype, int D, int heads_per_unit, hipStream_t stream);
 hipError_t launch_meanpool(const float *w, int d_model, int H, int G, int h, float *w_out, hipStream_t stream);
 hipError_t launch_fill_zero(void *ptr, size_t bytes, hipStream_t stream);

@@ -82,7 +82,9 @@ gqa_status gqa_workspace_init(void *workspace, size_t workspace_bytes, hipStream
  *             the new token's key/value must already be in the cache (the
  *             sketch appends before attending).  Values are clamped to
  *             [0, Lmax] on the device; 0 gives out[b] = 0.  Positions at or
- *             beyond seq_lens[b] are never read.
+ *             beyond seq_lens[b] never reach the output (a workgroup may
+ *             prefetch one 32-row tile below Lmax before the length is
+ *             known and discards it if it crosses the length).
  *   B, H, G, d, Lmax  B >= 0 (B = 0 is a no-op; pointers are then not
  *             checked), H >= 1, G >= 1, H % G == 0, d in {64, 128}, Lmax >= 1.
  *   scale     multiplies q . k before the softmax (1/sqrt(d) in the pages'

@@ -39,7 +39,8 @@ def env(monkeypatch):
                 monkeypatch.delenv(k, raising=False)
             else:
                 monkeypatch.setenv(k, str(v))
-    set_(GQA_KERNEL=None, GQA_CHUNK=None, GQA_TARGET_WGS=None, GQA_MAX_CHUNK=None, GQA_MERGE=None)
+    set_(GQA_KERNEL=None, GQA_CHUNK=None, GQA_TARGET_WGS=None, GQA_MAX_CHUNK=None, GQA_MERGE=None, GQA_WAVES=None,
+         GQA_CONTIG=None)
     return set_
 
 
@@ -137,6 +138,22 @@ def test_empty_batch(env):
     k = torch.empty((0, 2, 16, 64), dtype=torch.bfloat16, device=DEV)
     out = gqa.decode(q, k, k, torch.empty((0,), dtype=torch.int32, device=DEV), 0.125)
     assert out.shape == (0, 8, 64)
+
+
+@pytest.mark.parametrize("waves", [4, 8, 16])
+@pytest.mark.parametrize("contig", [0, 1])
+@pytest.mark.parametrize("case", [(3, 32, 8, 128, 3000, [3000, 1, 1777]), (4, 64, 8, 64, 2100, [2100, 2047, 33, 1000]),
+                                  (2, 48, 2, 128, 900, [900, 450])], ids=["d128_r4", "d64_r8", "d128_r24"])
+def test_launch_variants(env, waves, contig, case):
+    """Every workgroup size and tile order of the matrix-core kernel, single
+    and multi-split plans (first-tile prefetch used and discarded)."""
+    B, H, G, d, L, lens = case
+    q, k, v, lens_t, scale = rand_case(B, H, G, d, L, lens, "bf16", seed=31 + waves + contig)
+    ref = oracle_out(q, k, v, lens_t, scale)
+    for chunk in (None, 512, 1000):
+        env(GQA_WAVES=waves, GQA_CONTIG=contig, GQA_CHUNK=chunk)
+        out = run_gpu(q, k, v, lens_t, scale)
+        check(out, ref, "bf16", "waves=%d contig=%d chunk=%s %s" % (waves, contig, chunk, case[:5]))
 
 
 @pytest.mark.parametrize("kernel", ["default", "valu"])
