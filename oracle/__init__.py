@@ -49,17 +49,31 @@ class Oracle:
             ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
             ctypes.c_int, ctypes.c_double, ctypes.c_void_p, ctypes.c_int,
         ]
+        lib.gqa_oracle_decode_window.restype = ctypes.c_int
+        lib.gqa_oracle_decode_window.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+            ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_void_p, ctypes.c_int,
+        ]
+        lib.gqa_oracle_decode_append.restype = ctypes.c_int
+        lib.gqa_oracle_decode_append.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+            ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_void_p, ctypes.c_int,
+        ]
         lib.gqa_oracle_meanpool.restype = ctypes.c_int
         lib.gqa_oracle_meanpool.argtypes = [
             ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
         ]
         self._lib = lib
 
-    def decode(self, q, k_cache, v_cache, seq_lens, scale: float, nthreads: int | None = None) -> np.ndarray:
+    def decode(self, q, k_cache, v_cache, seq_lens, scale: float, nthreads: int | None = None,
+               window: int = 0) -> np.ndarray:
         """out[B,H,d] float64 for q[B,H,d], k/v[B,G,Lmax,d], seq_lens[B].
 
         Inputs may be numpy arrays (float32/float64) or CPU torch tensors
         (float32/float64/bfloat16); q, k and v must share one element type.
+        window > 0 attends only the last `window` positions of each sequence.
         """
         qa, elem_q = _host_array(q)
         ka, elem_k = _host_array(k_cache)
@@ -78,12 +92,40 @@ class Oracle:
         out = np.empty((B, H, d), dtype=np.float64)
         if nthreads is None:
             nthreads = len(os.sched_getaffinity(0))
-        rc = self._lib.gqa_oracle_decode(
+        rc = self._lib.gqa_oracle_decode_window(
             qa.ctypes.data, ka.ctypes.data, va.ctypes.data, elem_q, sl.ctypes.data,
-            B, H, G, d, Lmax, float(scale), out.ctypes.data, int(nthreads))
+            B, H, G, d, Lmax, int(window), float(scale), out.ctypes.data, int(nthreads))
         if rc != 0:
             raise ValueError("oracle decode rejected its arguments (rc=%d)" % rc)
         return out
+
+    def decode_append(self, q, k_new, v_new, k_cache, v_cache, seq_lens, scale: float,
+                      nthreads: int | None = None, window: int = 0):
+        """(out[B,H,d] float64, k_cache', v_cache'): append k_new/v_new [B,G,d] at
+        position len-1 of copies of the caches, then decode.  The returned
+        caches are numpy arrays in the input storage (bfloat16 as uint16 bits)."""
+        qa, e0 = _host_array(q)
+        kn, e1 = _host_array(k_new)
+        vn, e2 = _host_array(v_new)
+        ka, e3 = _host_array(k_cache)
+        va, e4 = _host_array(v_cache)
+        if len({e0, e1, e2, e3, e4}) != 1:
+            raise TypeError("all tensors must have one element type")
+        ka, va = ka.copy(), va.copy()
+        B, H, d = qa.shape
+        _, G, Lmax, _ = ka.shape
+        if kn.shape != (B, G, d) or vn.shape != (B, G, d):
+            raise ValueError("k_new/v_new must have shape [B,G,d]")
+        sl = np.ascontiguousarray(_to_numpy(seq_lens), dtype=np.int32)
+        out = np.empty((B, H, d), dtype=np.float64)
+        if nthreads is None:
+            nthreads = len(os.sched_getaffinity(0))
+        rc = self._lib.gqa_oracle_decode_append(
+            qa.ctypes.data, kn.ctypes.data, vn.ctypes.data, ka.ctypes.data, va.ctypes.data, e0, sl.ctypes.data,
+            B, H, G, d, Lmax, int(window), float(scale), out.ctypes.data, int(nthreads))
+        if rc != 0:
+            raise ValueError("oracle decode_append rejected its arguments (rc=%d)" % rc)
+        return out, ka, va
 
     def meanpool(self, w, H: int, G: int) -> np.ndarray:
         """w_out[d_model, G*h] float32 from w[d_model, H*h] float32."""
@@ -147,8 +189,12 @@ def get() -> Oracle:
     return _default
 
 
-def decode(q, k_cache, v_cache, seq_lens, scale, nthreads=None):
-    return get().decode(q, k_cache, v_cache, seq_lens, scale, nthreads)
+def decode(q, k_cache, v_cache, seq_lens, scale, nthreads=None, window=0):
+    return get().decode(q, k_cache, v_cache, seq_lens, scale, nthreads, window)
+
+
+def decode_append(q, k_new, v_new, k_cache, v_cache, seq_lens, scale, nthreads=None, window=0):
+    return get().decode_append(q, k_new, v_new, k_cache, v_cache, seq_lens, scale, nthreads, window)
 
 
 def meanpool(w, H, G):

@@ -47,13 +47,17 @@ typedef struct {
   int elem;
   const int32_t *seq_lens;
   int B, H, G, d, Lmax;
+  int window; /* > 0: attend only the last `window` cached positions */
   double scale;
   double *out;
   int nthreads, tid;
 } decode_job;
 
 /* One query head of one sequence: the decode-step block of the
- * Implementation sketch, over the positions 0 .. n-1 held in the cache. */
+ * Implementation sketch, over the positions lo .. n-1 held in the cache
+ * (lo = 0, or n - window for the sliding-window variant that the wikillm
+ * page's Variants section names for Mistral 7B: only the last `window`
+ * positions are attended). */
 static void decode_head(const decode_job *J, int b, int h, double *s) {
   const int r = J->H / J->G;      /* query heads per K/V head */
   const int g = h / r;            /* block assignment of heads to groups */
@@ -61,6 +65,8 @@ static void decode_head(const decode_job *J, int b, int h, double *s) {
   long n = J->seq_lens[b];
   if (n < 0) n = 0;
   if (n > J->Lmax) n = J->Lmax;
+  long lo = 0;
+  if (J->window > 0 && n > J->window) lo = n - J->window;
   double *o = J->out + ((size_t)b * J->H + h) * d;
   for (int c = 0; c < d; ++c) o[c] = 0.0;
   if (n == 0) return; /* empty cache: the empty weighted sum is zero */
@@ -69,7 +75,7 @@ static void decode_head(const decode_job *J, int b, int h, double *s) {
   const size_t kv_off = ((size_t)b * J->G + g) * (size_t)J->Lmax * d;
 
   /* scores[t] = scale * sum_i q[i] * K[t, i] */
-  for (long t = 0; t < n; ++t) {
+  for (long t = lo; t < n; ++t) {
     double acc = 0.0;
     for (int i = 0; i < d; ++i)
       acc += widen(J->q, q_off + i, J->elem) * widen(J->k, kv_off + (size_t)t * d + i, J->elem);
@@ -77,16 +83,16 @@ static void decode_head(const decode_job *J, int b, int h, double *s) {
   }
   /* softmax: subtracting the maximum leaves the quotient unchanged and only
    * keeps exp() in range */
-  double m = s[0];
-  for (long t = 1; t < n; ++t)
+  double m = s[lo];
+  for (long t = lo + 1; t < n; ++t)
     if (s[t] > m) m = s[t];
   double Z = 0.0;
-  for (long t = 0; t < n; ++t) {
+  for (long t = lo; t < n; ++t) {
     s[t] = exp(s[t] - m);
     Z += s[t];
   }
   /* out = sum_t (w[t] / Z) * V[t, :] */
-  for (long t = 0; t < n; ++t) {
+  for (long t = lo; t < n; ++t) {
     const double p = s[t] / Z;
     for (int c = 0; c < d; ++c)
       o[c] += p * widen(J->v, kv_off + (size_t)t * d + c, J->elem);
@@ -111,15 +117,15 @@ static void *decode_worker(void *arg) {
  * Returns 0, or -1 on a shape error (H % G != 0, non-positive sizes), -2 if a
  * worker could not allocate.
  */
-int gqa_oracle_decode(const void *q, const void *k_cache, const void *v_cache, int elem,
-                      const int32_t *seq_lens, int B, int H, int G, int d, int Lmax,
-                      double scale, double *out, int nthreads) {
-  if (B < 0 || H <= 0 || G <= 0 || d <= 0 || Lmax <= 0 || H % G != 0) return -1;
+int gqa_oracle_decode_window(const void *q, const void *k_cache, const void *v_cache, int elem,
+                             const int32_t *seq_lens, int B, int H, int G, int d, int Lmax, int window,
+                             double scale, double *out, int nthreads) {
+  if (B < 0 || H <= 0 || G <= 0 || d <= 0 || Lmax <= 0 || H % G != 0 || window < 0) return -1;
   if (elem < ORACLE_F32 || elem > ORACLE_F64) return -1;
   if (B == 0) return 0;
   if (nthreads < 1) nthreads = 1;
   if (nthreads > 256) nthreads = 256;
-  decode_job base = {q, k_cache, v_cache, elem, seq_lens, B, H, G, d, Lmax, scale, out, nthreads, 0};
+  decode_job base = {q, k_cache, v_cache, elem, seq_lens, B, H, G, d, Lmax, window, scale, out, nthreads, 0};
   decode_job jobs[256];
   pthread_t th[256];
   int rc = 0;
@@ -141,6 +147,44 @@ int gqa_oracle_decode(const void *q, const void *k_cache, const void *v_cache, i
       if (res) rc = -2;
     }
   return rc;
+}
+
+int gqa_oracle_decode(const void *q, const void *k_cache, const void *v_cache, int elem,
+                      const int32_t *seq_lens, int B, int H, int G, int d, int Lmax,
+                      double scale, double *out, int nthreads) {
+  return gqa_oracle_decode_window(q, k_cache, v_cache, elem, seq_lens, B, H, G, d, Lmax, 0, scale, out,
+                                  nthreads);
+}
+
+static size_t elem_size(int elem) { return elem == ORACLE_F64 ? 8 : (elem == ORACLE_F32 ? 4 : 2); }
+
+/*
+ * The decode-step block with its cache append: the new token's key and value
+ * (k_new, v_new [B,G,d]) are appended - written at position len-1 of each
+ * sequence's cache, where len = clamp(seq_lens[b], 0, Lmax) counts the new
+ * token - and then attended with the rest (gqa_oracle_decode_window).
+ * k_cache / v_cache are updated in place; len = 0 appends nothing.
+ */
+int gqa_oracle_decode_append(const void *q, const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                             int elem, const int32_t *seq_lens, int B, int H, int G, int d, int Lmax,
+                             int window, double scale, double *out, int nthreads) {
+  if (B < 0 || H <= 0 || G <= 0 || d <= 0 || Lmax <= 0 || H % G != 0 || window < 0) return -1;
+  if (elem < ORACLE_F32 || elem > ORACLE_F64) return -1;
+  const size_t es = elem_size(elem);
+  for (int b = 0; b < B; ++b) {
+    long n = seq_lens[b];
+    if (n < 0) n = 0;
+    if (n > Lmax) n = Lmax;
+    if (n == 0) continue;
+    for (int g = 0; g < G; ++g) {
+      const size_t dst = (((size_t)b * G + g) * (size_t)Lmax + (size_t)(n - 1)) * d;
+      const size_t src = ((size_t)b * G + g) * d;
+      memcpy((char *)k_cache + dst * es, (const char *)k_new + src * es, d * es);
+      memcpy((char *)v_cache + dst * es, (const char *)v_new + src * es, d * es);
+    }
+  }
+  return gqa_oracle_decode_window(q, k_cache, v_cache, elem, seq_lens, B, H, G, d, Lmax, window, scale, out,
+                                  nthreads);
 }
 
 /*

@@ -243,11 +243,89 @@ def pin_bf16_and_f32_storage(o):
         assert np.array_equal(a, b)
 
 
+def _sdpa_masked(q, k, v, scale, lo, n):
+    """torch SDPA for one sequence over positions lo .. n-1 (boolean mask), grouped."""
+    import torch
+    import torch.nn.functional as F
+    L = k.shape[1]
+    mask = torch.zeros(1, 1, 1, L, dtype=torch.bool)
+    mask[..., lo:n] = True
+    qt = torch.from_numpy(np.ascontiguousarray(q))[None, :, None, :]
+    kt = torch.from_numpy(np.ascontiguousarray(k))[None]
+    vt = torch.from_numpy(np.ascontiguousarray(v))[None]
+    o = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=scale, enable_gqa=True)
+    return o[0, :, 0, :].numpy()
+
+
+def pin_window_sdpa_mask(o):
+    """Sliding window: only positions max(0, len-W) .. len-1 are attended
+    (library SDPA with an explicit position mask)."""
+    rng = np.random.default_rng(41)
+    q, k, v, lens, sc = _rand_case(rng, 4, 8, 2, 8, 12, lens=[12, 7, 3, 1])
+    for W in (1, 2, 5, 7, 11, 12, 40):
+        out = o.decode(q, k, v, lens, sc, window=W)
+        for b in range(4):
+            n = int(lens[b])
+            ref = _sdpa_masked(q[b], k[b], v[b], sc, max(0, n - W), n)
+            np.testing.assert_allclose(out[b], ref, rtol=0, atol=1e-12, err_msg="W=%d b=%d" % (W, b))
+
+
+def pin_window_closed_forms(o):
+    """W = 1 gives the last value row exactly; W >= len gives the plain decode exactly."""
+    rng = np.random.default_rng(42)
+    q, k, v, lens, sc = _rand_case(rng, 3, 4, 2, 8, 9, lens=[9, 4, 1])
+    one = o.decode(q, k, v, lens, sc, window=1)
+    for b in range(3):
+        for h in range(4):
+            assert np.array_equal(one[b, h], v[b, h // 2, lens[b] - 1])
+    assert np.array_equal(o.decode(q, k, v, lens, sc, window=9), o.decode(q, k, v, lens, sc))
+    assert np.array_equal(o.decode(q, k, v, lens, sc, window=1000), o.decode(q, k, v, lens, sc))
+
+
+def _append_case(rng, B=3, H=8, G=2, d=8, L=10, lens=(10, 4, 1)):
+    q, k, v, lens, sc = _rand_case(rng, B, H, G, d, L, lens=list(lens))
+    k_new = rng.standard_normal((B, G, d))
+    v_new = rng.standard_normal((B, G, d))
+    return q, k, v, lens, sc, k_new, v_new
+
+
+def pin_append_updates_the_cache(o):
+    """The new key/value land at position len-1 of each sequence; nothing else changes."""
+    rng = np.random.default_rng(43)
+    q, k, v, lens, sc, kn, vn = _append_case(rng, lens=(10, 4, 1))
+    lens = np.array([10, 4, 0], np.int32)
+    _, k2, v2 = o.decode_append(q, kn, vn, k, v, lens, sc)
+    ek, ev = k.copy(), v.copy()
+    for b in range(2):
+        ek[b, :, lens[b] - 1] = kn[b]
+        ev[b, :, lens[b] - 1] = vn[b]
+    assert np.array_equal(k2, ek) and np.array_equal(v2, ev)
+
+
+def pin_append_matches_sdpa(o):
+    """Append then attend = library SDPA over the cache with row len-1
+    replaced by the new key/value; one position gives v_new exactly."""
+    rng = np.random.default_rng(44)
+    q, k, v, lens, sc, kn, vn = _append_case(rng, lens=(10, 5, 1))
+    for W in (0, 3):
+        out, _, _ = o.decode_append(q, kn, vn, k, v, lens, sc, window=W)
+        for b in range(3):
+            n = int(lens[b])
+            kk, vv = k[b].copy(), v[b].copy()
+            kk[:, n - 1] = kn[b]
+            vv[:, n - 1] = vn[b]
+            lo = max(0, n - W) if W else 0
+            np.testing.assert_allclose(out[b], _sdpa_masked(q[b], kk, vv, sc, lo, n), rtol=0, atol=1e-12)
+        for h in range(8):
+            assert np.array_equal(out[2, h], vn[2, h // 4])
+
+
 DECODE_PINS = [
     pin_sdpa_enable_gqa, pin_sdpa_replicated_heads, pin_mha_endpoint, pin_mqa_endpoint,
     pin_weights_are_softmax, pin_large_scores, pin_constant_values, pin_single_position,
     pin_zero_query, pin_permutation_invariance, pin_padding_never_read, pin_equal_queries,
     pin_empty_and_clamped_lengths, pin_golden_decode, pin_bf16_and_f32_storage,
+    pin_window_sdpa_mask, pin_window_closed_forms, pin_append_updates_the_cache, pin_append_matches_sdpa,
 ]
 
 

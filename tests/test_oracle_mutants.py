@@ -22,6 +22,12 @@ MUTANTS = [
     ("ignores_lengths", "long n = J->seq_lens[b];", "long n = J->Lmax;"),
     ("off_by_one_length", "long n = J->seq_lens[b];", "long n = J->seq_lens[b] - 1;"),
     ("no_max", "if (s[t] > m) m = s[t];", "if (s[t] < m) m = s[t];"),
+    ("window_one_short", "lo = n - J->window;", "lo = n - J->window + 1;"),
+    ("window_one_long", "lo = n - J->window;", "lo = n - J->window - 1;"),
+    ("window_ignored", "if (J->window > 0 && n > J->window)", "if (0)"),
+    ("append_wrong_row", "(size_t)Lmax + (size_t)(n - 1)) * d;", "(size_t)Lmax + (size_t)(n > 1 ? n - 2 : 0)) * d;"),
+    ("append_value_from_key", "(const char *)v_new + src * es", "(const char *)k_new + src * es"),
+    ("append_skipped", "memcpy((char *)k_cache + dst * es", "if (0) memcpy((char *)k_cache + dst * es"),
     ("pool_divides_by_G", "(float)(acc / (double)r)", "(float)(acc / (double)G)"),
     ("pool_interleaved_columns", "acc += (double)wr[(size_t)i * h + c];", "acc += (double)wr[(size_t)c * H + i];"),
     ("pool_float_accumulator", "double acc = (double)wr[(size_t)(g * r) * h + c];",
