@@ -41,11 +41,17 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def alg_bytes(w, seq_lens) -> int:
-    """K+V bytes of the attended positions plus q and out (element bytes e)."""
+def alg_bytes(w, seq_lens, variant: str = "decode", window: int = 0) -> int:
+    """K+V bytes of the attended positions plus q and out (element bytes e);
+    with a window only the last `window` positions count; the cache append
+    adds the new rows written into the cache (their reads replace cache reads)."""
     e = 4 if w.dtype == "f32" else 2
-    n = int(seq_lens.to("cpu").clamp(0, w.Lmax).sum())
-    return 2 * w.G * n * w.d * e + 2 * w.B * w.H * w.d * e
+    lens = seq_lens.to("cpu").clamp(0, w.Lmax)
+    if window > 0:
+        lens = lens.clamp(max=window)
+    n = int(lens.sum())
+    extra = 2 * w.B * w.G * w.d * e if variant == "append" else 0
+    return 2 * w.G * n * w.d * e + 2 * w.B * w.H * w.d * e + extra
 
 
 def load_traffic(workload_name: str):
@@ -111,10 +117,17 @@ def run_bench(args):
     gqa.load_library()
     kv_bytes = 2 * w.B * w.G * w.Lmax * w.d * (4 if w.dtype == "f32" else 2)
     rot = args.rotate if args.rotate else max(1, math.ceil((1 << 30) / kv_bytes))
+    window = args.window if args.variant in ("window", "append") else 0
     sets, decs = [], []
     for i in range(rot):
         q, k, v, lens = wl.make_inputs(w, dev, pad="none", seed_offset=i)
-        dec = gqa.Decoder(q, k, v, lens, w.scale)
+        if args.variant == "append":
+            gen = torch.Generator(dev).manual_seed(w.seed + 7 * i)
+            kn = torch.randn((w.B, w.G, w.d), generator=gen, device=dev).to(k.dtype)
+            vn = torch.randn((w.B, w.G, w.d), generator=gen, device=dev).to(k.dtype)
+            dec = gqa.Decoder(q, k, v, lens, w.scale, window=window, k_new=kn, v_new=vn)
+        else:
+            dec = gqa.Decoder(q, k, v, lens, w.scale, window=window)
         sets.append((q, k, v, lens))
         decs.append(dec)
     torch.cuda.synchronize()
@@ -142,10 +155,10 @@ def run_bench(args):
     code = gqa.GQA_F32 if w.dtype == "f32" else gqa.GQA_BF16
     split = gqa.decode_workspace_size(w.B, w.H, w.G, w.d, w.Lmax, code) > 0
     kernels_per_step = 2 if split and os.environ.get("GQA_MERGE") == "kernel" else 1
-    ab = alg_bytes(w, sets[0][3])  # every rotation set has the same lengths
+    ab = alg_bytes(w, sets[0][3], args.variant, window)  # every rotation set has the same lengths
     achieved = ab / (avg_kernel_ms * 1e-3) / 1e9
     ms_per_step = wall * 1e3 / K
-    traffic = load_traffic(w.name)
+    traffic = load_traffic(w.name) if args.variant == "decode" else None
 
     line = {
         "metric": METRIC,
@@ -161,7 +174,7 @@ def run_bench(args):
         "dtype": w.dtype,
         "data": "synthetic (seeded Gaussian caches)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "G": w.G, "d": w.d, "Lmax": w.Lmax,
-                   "ragged": w.ragged, "rotation_sets": rot,
+                   "ragged": w.ragged, "rotation_sets": rot, "variant": args.variant, "window": window,
                    "kernel": ["valu", "mfma"][kind], "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic},
@@ -170,7 +183,7 @@ def run_bench(args):
         "kernels_per_step": kernels_per_step,
         "hbm_gbps_wall": ab / (ms_per_step * 1e-3) / 1e9,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.variant == "decode":
         q, k, v, lens = sets[0]
         out = decs[0]().clone()
         torch.cuda.synchronize()
@@ -264,6 +277,9 @@ def main():
     ap.add_argument("--workload", default="mistral7b_bf16_B16_H32_G8_d128_L4096")
     ap.add_argument("--rotate", type=int, default=0, help="input sets cycled through (default: >= 1 GiB of caches)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--variant", choices=["decode", "append", "window"], default="decode",
+                    help="decode (default), decode with the cache append, or sliding-window decode")
+    ap.add_argument("--window", type=int, default=4096, help="window for --variant window/append (0: none)")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time to aim for")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--summarize-rocprof", metavar="DIR")

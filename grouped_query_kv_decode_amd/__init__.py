@@ -9,6 +9,8 @@ Entry points (same names as the C ABI, without the ``gqa_`` prefix):
     decode(q, k_cache, v_cache, seq_lens, scale, out=None, workspace=None)
     decode_workspace_size(B, H, G, d, Lmax, dtype)
     decode_phase(phase, ...)           (split kernel / merge kernel separately)
+    decode_window(q, k_cache, v_cache, seq_lens, scale, window, ...)
+    decode_append(q, k_new, v_new, k_cache, v_cache, seq_lens, scale, window=0, ...)
     workspace_init(workspace)
     meanpool_kv(w, H, G, out=None)
     decode_kernel_kind(B, H, G, d, Lmax, dtype)
@@ -19,7 +21,7 @@ import ctypes
 import os
 
 __all__ = [
-    "GQAError", "decode", "decode_phase", "decode_workspace_size", "workspace_init", "meanpool_kv",
+    "GQAError", "decode", "decode_phase", "decode_window", "decode_append", "decode_workspace_size", "workspace_init", "meanpool_kv",
     "decode_kernel_kind", "status_string", "library_path", "load_library", "Decoder",
     "GQA_F32", "GQA_BF16",
 ]
@@ -33,7 +35,8 @@ STATUS_NAMES = {
     5: "GQA_ERR_WORKSPACE", 6: "GQA_ERR_SCALE", 7: "GQA_ERR_HIP", 8: "GQA_ERR_SIZE",
 }
 EXPORTED = [
-    "gqa_decode_workspace_size", "gqa_workspace_init", "gqa_decode", "gqa_decode_phase", "gqa_meanpool_kv",
+    "gqa_decode_workspace_size", "gqa_workspace_init", "gqa_decode", "gqa_decode_phase", "gqa_decode_window",
+    "gqa_decode_append", "gqa_meanpool_kv",
     "gqa_status_string", "gqa_last_hip_error", "gqa_decode_kernel_kind",
 ]
 
@@ -71,6 +74,11 @@ def load_library(path: str | None = None):
     lib.gqa_decode_phase.argtypes = [ci, vp, vp, vp, vp, ci, ci, ci, ci, ci, ctypes.c_float, ci, vp, vp, sz, vp]
     lib.gqa_decode.restype = ci
     lib.gqa_decode.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, ci, ctypes.c_float, ci, vp, vp, sz, vp]
+    lib.gqa_decode_window.restype = ci
+    lib.gqa_decode_window.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ctypes.c_float, ci, vp, vp, sz, vp]
+    lib.gqa_decode_append.restype = ci
+    lib.gqa_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ctypes.c_float, ci, vp, vp, sz,
+                                      vp]
     lib.gqa_meanpool_kv.restype = ci
     lib.gqa_meanpool_kv.argtypes = [vp, ci, ci, ci, ci, vp, vp]
     lib.gqa_status_string.restype = ctypes.c_char_p
@@ -135,7 +143,7 @@ def _workspace_for(nbytes: int, device):
     return ws
 
 
-def _prepare(q, k_cache, v_cache, seq_lens, scale, out, workspace):
+def _prepare(q, k_cache, v_cache, seq_lens, scale, out, workspace, window=0):
     """Checks the tensors and returns (ctypes argument tuple without the stream, out, workspace)."""
     import torch
     B, H, d = q.shape
@@ -156,7 +164,7 @@ def _prepare(q, k_cache, v_cache, seq_lens, scale, out, workspace):
         out = torch.empty((B, H, d), dtype=q.dtype, device=q.device)
     elif tuple(out.shape) != (B, H, d) or out.dtype != q.dtype or not out.is_contiguous() or out.device != q.device:
         raise ValueError("out must be a contiguous [B,H,d] tensor of q's dtype on q's GPU")
-    need = decode_workspace_size(B, H, G, d, Lmax, code)
+    need = decode_workspace_size(B, H, G, d, min(Lmax, window) if window > 0 else Lmax, code)
     if workspace is None and need > 0:
         workspace = _workspace_for(need, q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
@@ -189,26 +197,73 @@ def decode_phase(phase: int, q, k_cache, v_cache, seq_lens, scale: float, out=No
     return out
 
 
+def decode_window(q, k_cache, v_cache, seq_lens, scale: float, window: int, out=None, workspace=None):
+    """Sliding-window decode: each sequence attends its last `window` positions."""
+    args, out, _ = _prepare(q, k_cache, v_cache, seq_lens, scale, out, workspace, window=int(window))
+    a = args[:9] + (int(window),) + args[9:]
+    st = load_library().gqa_decode_window(*a, _stream_handle(q.device))
+    if st:
+        raise GQAError(st, "gqa_decode_window")
+    return out
+
+
+def _check_new(k_new, v_new, k_cache):
+    B, G, _, d = k_cache.shape
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        if tuple(t.shape) != (B, G, d) or t.dtype != k_cache.dtype or not t.is_contiguous() \
+                or t.device != k_cache.device:
+            raise ValueError("%s must be a contiguous [B,G,d] tensor of the cache dtype on its GPU" % name)
+
+
+def decode_append(q, k_new, v_new, k_cache, v_cache, seq_lens, scale: float, window: int = 0, out=None,
+                  workspace=None):
+    """Write k_new/v_new [B,G,d] at position seq_lens[b]-1 of the caches (in
+    place), then decode over the updated caches (window > 0: sliding window)."""
+    _check_new(k_new, v_new, k_cache)
+    args, out, _ = _prepare(q, k_cache, v_cache, seq_lens, scale, out, workspace, window=int(window))
+    a = (args[0], k_new.data_ptr(), v_new.data_ptr()) + args[1:9] + (int(window),) + args[9:]
+    st = load_library().gqa_decode_append(*a, _stream_handle(q.device))
+    if st:
+        raise GQAError(st, "gqa_decode_append")
+    return out
+
+
 class Decoder:
     """A decode call bound to fixed tensors and to the stream current at
     construction; each call() is one C-ABI call with pre-marshalled
     arguments (for tight loops: serving steps, benchmarks)."""
 
-    def __init__(self, q, k_cache, v_cache, seq_lens, scale: float, out=None, workspace=None):
-        self._keep = (q, k_cache, v_cache, seq_lens)
-        self._args, self.out, self.workspace = _prepare(q, k_cache, v_cache, seq_lens, scale, out, workspace)
-        self._args = self._args + (_stream_handle(q.device),)
-        self._fn = load_library().gqa_decode
-        self._phase = load_library().gqa_decode_phase
+    def __init__(self, q, k_cache, v_cache, seq_lens, scale: float, out=None, workspace=None, window: int = 0,
+                 k_new=None, v_new=None):
+        self._keep = (q, k_cache, v_cache, seq_lens, k_new, v_new)
+        args, self.out, self.workspace = _prepare(q, k_cache, v_cache, seq_lens, scale, out, workspace,
+                                                  window=int(window))
+        stream = (_stream_handle(q.device),)
+        lib = load_library()
+        self._phase_args = args + stream
+        if k_new is not None:
+            _check_new(k_new, v_new, k_cache)
+            self._fn, self._name = lib.gqa_decode_append, "gqa_decode_append"
+            self._args = (args[0], k_new.data_ptr(), v_new.data_ptr()) + args[1:9] + (int(window),) + args[9:] + stream
+        elif window > 0:
+            self._fn, self._name = lib.gqa_decode_window, "gqa_decode_window"
+            self._args = args[:9] + (int(window),) + args[9:] + stream
+        else:
+            self._fn, self._name = lib.gqa_decode, "gqa_decode"
+            self._args = args + stream
+        self._phase = lib.gqa_decode_phase
+        self._plain = k_new is None and window <= 0
 
     def __call__(self):
         st = self._fn(*self._args)
         if st:
-            raise GQAError(st, "gqa_decode")
+            raise GQAError(st, self._name)
         return self.out
 
     def phase(self, phase: int):
-        st = self._phase(phase, *self._args)
+        if not self._plain:
+            raise ValueError("phases are available for plain decode only")
+        st = self._phase(phase, *self._phase_args)
         if st:
             raise GQAError(st, "gqa_decode_phase")
         return self.out

@@ -162,20 +162,32 @@ gqa_status gqa_workspace_init(void *workspace, size_t workspace_bytes, hipStream
   return e == hipSuccess ? GQA_OK : hip_fail(e);
 }
 
-gqa_status gqa_decode_phase(int phase, const void *q, const void *k_cache, const void *v_cache,
-                            const int32_t *seq_lens, int B, int H, int G, int d, int Lmax, float scale,
-                            gqa_dtype dtype, void *out, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared body of the decode entry points.  k_new / v_new (both or neither)
+// switch on the cache append; window > 0 the sliding window.
+gqa_status decode_impl(int phase, const void *q, const void *k_new, const void *v_new, const void *k_cache,
+                       const void *v_cache, const int32_t *seq_lens, int B, int H, int G, int d, int Lmax,
+                       int window, float scale, gqa_dtype dtype, void *out, void *workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
   if (phase != 0 && phase != 1 && phase != 2) return GQA_ERR_UNSUPPORTED;
   gqa_status st = check_shape(B, H, G, d, Lmax, dtype);
   if (st != GQA_OK) return st;
+  if (window < 0) return GQA_ERR_SHAPE;
   if (B == 0) return GQA_OK;
   if (!q || !k_cache || !v_cache || !seq_lens || !out) return GQA_ERR_NULL;
+  if ((k_new == nullptr) != (v_new == nullptr)) return GQA_ERR_NULL;
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) || !aligned(seq_lens, 4))
     return GQA_ERR_ALIGN;
+  if (k_new && (!aligned(k_new, 16) || !aligned(v_new, 16))) return GQA_ERR_ALIGN;
   const double sl2 = (double)scale * 1.4426950408889634;
   if (!isfinite(scale) || !isfinite((float)sl2)) return GQA_ERR_SCALE;
+  // a window shorter than the cache plans splits over the window only
+  const int Leff = (window > 0 && window < Lmax) ? window : Lmax;
   Plan pl;
-  st = make_plan(B, H, G, d, Lmax, dtype, &pl);
+  st = make_plan(B, H, G, d, Leff, dtype, &pl);
   if (st != GQA_OK) return st;
   if (pl.ws_bytes > 0) {
     if (!workspace) return GQA_ERR_NULL;
@@ -187,6 +199,8 @@ gqa_status gqa_decode_phase(int phase, const void *q, const void *k_cache, const
   p.q = q;
   p.k = k_cache;
   p.v = v_cache;
+  p.k_new = k_new;
+  p.v_new = v_new;
   p.seq_lens = seq_lens;
   p.out = out;
   char *ws = static_cast<char *>(workspace);
@@ -199,6 +213,7 @@ gqa_status gqa_decode_phase(int phase, const void *q, const void *k_cache, const
   p.H = H;
   p.G = G;
   p.Lmax = Lmax;
+  p.window = window;
   p.r = H / G;
   p.S = pl.S;
   p.chunk = pl.chunk;
@@ -218,11 +233,44 @@ gqa_status gqa_decode_phase(int phase, const void *q, const void *k_cache, const
   return GQA_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+gqa_status gqa_decode_phase(int phase, const void *q, const void *k_cache, const void *v_cache,
+                            const int32_t *seq_lens, int B, int H, int G, int d, int Lmax, float scale,
+                            gqa_dtype dtype, void *out, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  return decode_impl(phase, q, nullptr, nullptr, k_cache, v_cache, seq_lens, B, H, G, d, Lmax, 0, scale, dtype, out,
+                     workspace, workspace_bytes, stream);
+}
+
 gqa_status gqa_decode(const void *q, const void *k_cache, const void *v_cache, const int32_t *seq_lens, int B, int H,
                       int G, int d, int Lmax, float scale, gqa_dtype dtype, void *out, void *workspace,
                       size_t workspace_bytes, hipStream_t stream) {
-  return gqa_decode_phase(0, q, k_cache, v_cache, seq_lens, B, H, G, d, Lmax, scale, dtype, out, workspace,
-                          workspace_bytes, stream);
+  return decode_impl(0, q, nullptr, nullptr, k_cache, v_cache, seq_lens, B, H, G, d, Lmax, 0, scale, dtype, out,
+                     workspace, workspace_bytes, stream);
+}
+
+gqa_status gqa_decode_window(const void *q, const void *k_cache, const void *v_cache, const int32_t *seq_lens,
+                             int B, int H, int G, int d, int Lmax, int window, float scale, gqa_dtype dtype,
+                             void *out, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  const gqa_status st = check_shape(B, H, G, d, Lmax, dtype);
+  if (st != GQA_OK) return st;
+  if (window < 1) return GQA_ERR_SHAPE;
+  return decode_impl(0, q, nullptr, nullptr, k_cache, v_cache, seq_lens, B, H, G, d, Lmax, window, scale, dtype,
+                     out, workspace, workspace_bytes, stream);
+}
+
+gqa_status gqa_decode_append(const void *q, const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                             const int32_t *seq_lens, int B, int H, int G, int d, int Lmax, int window, float scale,
+                             gqa_dtype dtype, void *out, void *workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+  const gqa_status st = check_shape(B, H, G, d, Lmax, dtype);
+  if (st != GQA_OK) return st;
+  if (window < 0) return GQA_ERR_SHAPE;
+  if (B > 0 && (!k_new || !v_new)) return GQA_ERR_NULL;
+  return decode_impl(0, q, k_new, v_new, k_cache, v_cache, seq_lens, B, H, G, d, Lmax, window, scale, dtype, out,
+                     workspace, workspace_bytes, stream);
 }
 
 gqa_status gqa_meanpool_kv(const float *w, int d_model, int H, int G, int h, float *w_out, hipStream_t stream) {

@@ -142,19 +142,30 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma(DecodeParams p) {
   // out to be inside the split, otherwise the tile is loaded again below.
   // Limited to the leading splits, so workgroups of splits past a short
   // sequence's end waste little.
+  // (Only without a window: with one, where splits start depends on the length.)
   const int t_first = t0 + 32 * wave;
-  const bool spec = !p.contig && (s == 0 || p.S <= 2) && t_first + 32 <= min(t0 + p.chunk, p.Lmax);
+  const bool spec =
+      !p.contig && p.window <= 0 && (s == 0 || p.S <= 2) && t_first + 32 <= min(t0 + p.chunk, p.Lmax);
   Tile T_first;
   if (spec) load_full(T_first, t_first);
 
   const int n = clamp_len(p, b);
-  const int nsplit = num_splits(n, p.chunk);
+  const int lo = window_lo(p, n);
+  const int nsplit = num_splits(n - lo, p.chunk);
   if (s >= nsplit) return;
   if (n == 0) {
     write_zero_heads<__bf16, D>(p, b, head0, p.r);
     return;
   }
-  const int t1 = min(t0 + p.chunk, n);
+  const int ts = lo + t0;  // this split: positions [ts, t1)
+  const int t1 = min(ts + p.chunk, n);
+  // With a cache append, position n-1 comes from k_new / v_new: whole tiles
+  // must end before it, the tile holding it takes the per-row path.
+  const bool append = p.k_new != nullptr;
+  const int t_full = append ? min(t1, n - 1) : t1;
+  if (append && s == nsplit - 1) append_row<__bf16, D>(p, b, g, n);
+  const __bf16 *knew = append ? static_cast<const __bf16 *>(p.k_new) + ((size_t)b * p.G + g) * D : nullptr;
+  const __bf16 *vnew = append ? static_cast<const __bf16 *>(p.v_new) + ((size_t)b * p.G + g) * D : nullptr;
 
   f32x4 o[HB][DB];
   float m[HB], l[HB];
@@ -167,20 +178,21 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma(DecodeParams p) {
   }
 
   // The last tile of a split: rows past the split end are clamped to its last
-  // row (never past the sequence length) and masked out of the softmax.
+  // row (never past the sequence length) and masked out of the softmax; the
+  // appended row n-1 is read from k_new / v_new.
   auto load_tail = [&](Tile &T, int tt) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int t = tt + 8 * (nn >> 2) + 4 * h + (nn & 3);
-      const size_t row = (size_t)min(t, t1 - 1);
+      const int t = min(tt + 8 * (nn >> 2) + 4 * h + (nn & 3), t1 - 1);
+      const __bf16 *src = (append && t == n - 1) ? knew : kbase + (size_t)t * D;
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-        T.kA[h][kb] = *reinterpret_cast<const u32x4 *>(kbase + row * D + 8 * c + kb * 32);
+      for (int kb = 0; kb < KB; ++kb) T.kA[h][kb] = *reinterpret_cast<const u32x4 *>(src + 8 * c + kb * 32);
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const size_t row = (size_t)min(tt + 8 * c + u, t1 - 1);
-      T.vR[u] = *reinterpret_cast<const VRow *>(vbase + row * D + VPL * nn);
+      const int t = min(tt + 8 * c + u, t1 - 1);
+      const __bf16 *src = (append && t == n - 1) ? vnew : vbase + (size_t)t * D;
+      T.vR[u] = *reinterpret_cast<const VRow *>(src + VPL * nn);
     }
   };
   // Scores, softmax weights and the weighted V sum of one tile.  The running
@@ -237,22 +249,22 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma(DecodeParams p) {
   // per iteration (their loads are issued together).
   int tt, te, kStride;
   if (p.contig) {
-    const int ntiles = (t1 - t0 + 31) / 32;
+    const int ntiles = (t1 - ts + 31) / 32;
     const int per = (ntiles + NW - 1) / NW;
-    tt = t0 + 32 * per * wave;
+    tt = ts + 32 * per * wave;
     te = min(t1, tt + 32 * per);
     kStride = 32;
   } else {
-    tt = t0 + 32 * wave;
+    tt = ts + 32 * wave;
     te = t1;
     kStride = 32 * NW;
-    if (spec && tt + 32 <= t1) {  // the prefetched first tile is whole: use it
+    if (spec && tt + 32 <= t_full) {  // the prefetched first tile is whole: use it
       compute(T_first, tt, false);
       tt += kStride;
     }
   }
   if (TPI == 2) {
-    for (; tt + kStride + 32 <= te; tt += 2 * kStride) {
+    for (; tt + kStride + 32 <= min(te, t_full); tt += 2 * kStride) {
       Tile T0, T1;
       load_full(T0, tt);
       load_full(T1, tt + kStride);
@@ -262,10 +274,10 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma(DecodeParams p) {
   }
   for (; tt < te; tt += kStride) {
     Tile T;
-    if (tt + 32 <= t1) {
+    if (tt + 32 <= t_full) {
       load_full(T, tt);
       compute(T, tt, false);
-    } else {  // only the split's last tile can be partial
+    } else {  // the split's last tile (partial, or holding the appended row)
       load_tail(T, tt);
       compute(T, tt, true);
     }

@@ -72,7 +72,8 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeParams p) {
   const int b = id / p.G;
 
   const int n = clamp_len(p, b);
-  const int nsplit = num_splits(n, p.chunk);
+  const int lo = window_lo(p, n);
+  const int nsplit = num_splits(n - lo, p.chunk);
   if (s >= nsplit) return;
   const int jbase = hc * RC;
   const int nh = min(RC, p.r - jbase);
@@ -81,7 +82,11 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeParams p) {
     write_zero_heads<T, D>(p, b, head0, nh);
     return;
   }
-  const int t0 = s * p.chunk, t1 = min(t0 + p.chunk, n);
+  const int t0 = lo + s * p.chunk, t1 = min(t0 + p.chunk, n);
+  // Cache append: position n-1 is read from k_new / v_new and written into
+  // the cache by one workgroup of the last split.
+  const bool append = p.k_new != nullptr;
+  if (append && s == nsplit - 1 && hc == 0) append_row<T, D>(p, b, g, n);
 
   // Query rows of the served heads, pre-multiplied by scale*log2(e).
   float qf[RC][EPL];
@@ -102,6 +107,8 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeParams p) {
   const size_t slab = ((size_t)b * p.G + g) * (size_t)p.Lmax * D;
   const T *kp = static_cast<const T *>(p.k) + slab + sub * EPL;
   const T *vp = static_cast<const T *>(p.v) + slab + sub * EPL;
+  const T *knew = append ? static_cast<const T *>(p.k_new) + ((size_t)b * p.G + g) * D + sub * EPL : nullptr;
+  const T *vnew = append ? static_cast<const T *>(p.v_new) + ((size_t)b * p.G + g) * D + sub * EPL : nullptr;
 
   float m[RC], l[RC], o[RC][EPL];
 #pragma unroll
@@ -119,9 +126,10 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeParams p) {
     for (int u = 0; u < U; ++u) {
       const int t = tb + u * NRG + rg;
       ok[u] = t < t1;
-      const size_t row = (size_t)(ok[u] ? t : t1 - 1);  // never past the length
-      kr[u] = *reinterpret_cast<const uint4 *>(kp + row * D);
-      vr[u] = *reinterpret_cast<const uint4 *>(vp + row * D);
+      const int row = ok[u] ? t : t1 - 1;  // never past the length
+      const bool fresh = append && row == n - 1;
+      kr[u] = *reinterpret_cast<const uint4 *>(fresh ? knew : kp + (size_t)row * D);
+      vr[u] = *reinterpret_cast<const uint4 *>(fresh ? vnew : vp + (size_t)row * D);
     }
     float sc[U][RC];
 #pragma unroll

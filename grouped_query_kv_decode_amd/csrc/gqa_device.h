@@ -18,6 +18,8 @@ struct DecodeParams {
   const void *q;           // [B, H, D]
   const void *k;           // [B, G, Lmax, D]
   const void *v;           // [B, G, Lmax, D]
+  const void *k_new;       // [B, G, D] new token's keys (cache append), or null
+  const void *v_new;       // [B, G, D] new token's values, or null
   const int32_t *seq_lens; // [B]
   void *out;               // [B, H, D]
   float *ws_o;             // [B, H, S, D]  un-normalised split outputs
@@ -26,6 +28,7 @@ struct DecodeParams {
   int fused;               // 1: the last split of a unit merges; 0: a merge kernel follows
   int contig;              // matrix-core kernel: contiguous per-wave tile runs instead of interleaved tiles
   int B, H, G, Lmax;
+  int window;              // > 0: attend only the last `window` positions
   int r;                   // query heads per K/V head, H / G
   int S;                   // splits per (b, g) in the grid
   int chunk;               // positions per split
@@ -48,6 +51,28 @@ __device__ __forceinline__ int clamp_len(const DecodeParams &p, int b) {
 }
 
 __device__ __forceinline__ int num_splits(int n, int chunk) { return n > 0 ? (n + chunk - 1) / chunk : 1; }
+
+// First attended position: 0, or len - window under a sliding window.  Splits
+// cover [lo, len) from lo on.
+__device__ __forceinline__ int window_lo(const DecodeParams &p, int n) {
+  return (p.window > 0 && n > p.window) ? n - p.window : 0;
+}
+
+// Cache append (the decode-step block appends the new token's key and value,
+// then attends): the workgroup whose split holds position n-1 writes the new
+// row into the cache.  Threads 0 .. D*sizeof(T)/16-1 move 16 bytes each.
+template <typename T, int D>
+__device__ __forceinline__ void append_row(const DecodeParams &p, int b, int g, int n) {
+  constexpr int kLanes = D * (int)sizeof(T) / 16;
+  if ((int)threadIdx.x < kLanes) {
+    const size_t src = ((size_t)b * p.G + g) * D + threadIdx.x * (16 / sizeof(T));
+    const size_t dst = (((size_t)b * p.G + g) * (size_t)p.Lmax + (size_t)(n - 1)) * D + threadIdx.x * (16 / sizeof(T));
+    *reinterpret_cast<uint4 *>(static_cast<T *>(const_cast<void *>(p.k)) + dst) =
+        *reinterpret_cast<const uint4 *>(static_cast<const T *>(p.k_new) + src);
+    *reinterpret_cast<uint4 *>(static_cast<T *>(const_cast<void *>(p.v)) + dst) =
+        *reinterpret_cast<const uint4 *>(static_cast<const T *>(p.v_new) + src);
+  }
+}
 
 template <typename T> struct Store;
 template <> struct Store<float> {

@@ -21,7 +21,8 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p, int heads_pe
   const int units_per_b = p.H / heads_per_unit;
   const int b = blockIdx.x / units_per_b;
   const int head0 = (blockIdx.x % units_per_b) * heads_per_unit;
-  const int nsplit = num_splits(clamp_len(p, b), p.chunk);
+  const int n = clamp_len(p, b);
+  const int nsplit = num_splits(n - window_lo(p, n), p.chunk);
   if (nsplit <= 1) return;  // written directly by the split kernel
   merge_heads<T, D>(p, b, head0, heads_per_unit, nsplit);
 }

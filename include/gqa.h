@@ -124,6 +124,42 @@ gqa_status gqa_decode_phase(int phase, const void *q, const void *k_cache, const
                             gqa_dtype dtype, void *out, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Sliding-window decode: as gqa_decode, but sequence b attends only its last
+ * `window` cached positions, [max(0, len_b - window), len_b).  The wikillm
+ * page "Grouped-query attention (GQA)" (Variants, decoder-only models) notes
+ * that Mistral 7B pairs GQA with sliding-window attention, which the GQA
+ * paper does not cover; this is the plain reading of a window of `window`
+ * positions ending at the new token.
+ *   window >= 1 (GQA_ERR_SHAPE otherwise).  Positions before the window are
+ *   not read.  Workspace: gqa_decode_workspace_size(B, H, G, d,
+ *   min(Lmax, window), dtype) bytes; other arguments as for gqa_decode.
+ */
+gqa_status gqa_decode_window(const void *q, const void *k_cache, const void *v_cache, const int32_t *seq_lens,
+                             int B, int H, int G, int d, int Lmax, int window, float scale, gqa_dtype dtype,
+                             void *out, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Decode with the cache append of the decode-step block (wikillm "Grouped-
+ * query attention (GQA)", Implementation sketch: the new token's G key heads
+ * and G value heads are appended to the cache, then attended) in one launch:
+ *   k_new, v_new  [B, G, d] dtype, device (16-byte aligned): the new token's
+ *                 keys and values.
+ *   k_cache, v_cache  [B, G, Lmax, d], updated in place: row len_b - 1 of each
+ *                 (b, g) slab receives k_new[b, g] / v_new[b, g], where
+ *                 len_b = clamp(seq_lens[b], 0, Lmax) counts the new token;
+ *                 nothing else in the caches is written.  len_b = 0 appends
+ *                 nothing and gives out[b] = 0.
+ *   window        0 for none, else as for gqa_decode_window (workspace sized
+ *                 with min(Lmax, window) then).
+ * The output equals gqa_decode (or gqa_decode_window) over the updated
+ * caches.  Other arguments as for gqa_decode.
+ */
+gqa_status gqa_decode_append(const void *q, const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                             const int32_t *seq_lens, int B, int H, int G, int d, int Lmax, int window, float scale,
+                             gqa_dtype dtype, void *out, void *workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
+/*
  * The pages' checkpoint conversion step, numeric core only: wikillm
  * "Grouped-query attention (GQA)", Implementation sketch (conversion block)
  * and Variants ("Converted and uptrained checkpoints"): the key (or value)

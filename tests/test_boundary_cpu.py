@@ -144,6 +144,24 @@ def test_phase_argument(lib):
     assert lib.gqa_decode_phase(2, None, None, None, None, 0, 8, 2, 128, 512, 0.125, BF16, None, None, 0, None) == OK
 
 
+def test_window_and_append_arguments(lib):
+    win = lambda W, **kw: lib.gqa_decode_window(kw.get("q", P), P, P, P, kw.get("B", 2), kw.get("H", 8), 2, 128,
+                                                512, W, 0.125, BF16, P, P, 1 << 30, None)
+    assert win(0) == SHAPE
+    assert win(-3) == SHAPE
+    assert win(5, H=7) == SHAPE
+    assert win(5, B=0, q=None) == OK
+    assert win(5, q=None) == NULL
+    app = lambda kn=P, vn=P, W=0, B=2, H=8: lib.gqa_decode_append(P, kn, vn, P, P, P, B, H, 2, 128, 512, W, 0.125,
+                                                                  BF16, P, P, 1 << 30, None)
+    assert app(kn=None) == NULL
+    assert app(vn=None) == NULL
+    assert app(kn=P + 8) == ALIGN
+    assert app(W=-1) == SHAPE
+    assert app(H=7) == SHAPE
+    assert app(kn=None, vn=None, B=0) == OK
+
+
 def test_binding_rejects_bad_tensors():
     import torch
     q = torch.zeros(2, 8, 64)

@@ -247,6 +247,79 @@ def test_fused_merge_matches_merge_kernel(env, kernel):
             assert torch.equal(o, ref)
 
 
+# --------------------------------------------------------------- sliding window and cache append
+
+WIN_CASES = [
+    (4, 32, 8, 128, 3000, [3000, 2500, 100, 1]),
+    (3, 64, 8, 64, 2100, [2100, 33, 1500]),
+    (2, 12, 4, 128, 700, [700, 64]),   # r = 3
+]
+
+
+@pytest.mark.parametrize("case", WIN_CASES, ids=["d128_r4", "d64_r8", "d128_r3"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("kernel", ["default", "valu"])
+def test_window_parity(env, case, dtype, kernel):
+    B, H, G, d, L, lens = case
+    q, k, v, lens_t, scale = rand_case(B, H, G, d, L, lens, dtype, seed=51 + d)
+    for chunk in (None, 128):
+        env(GQA_KERNEL=None if kernel == "default" else kernel, GQA_CHUNK=chunk)
+        for W in (1, 31, 32, 33, 511, 1000, 5000):
+            out = gqa.decode_window(q, k, v, lens_t, scale, W)
+            torch.cuda.synchronize()
+            ref = oracle.decode(q.cpu(), k.cpu(), v.cpu(), lens_t.cpu(), scale, window=W)
+            check(out, ref, dtype, "window=%d chunk=%s %s" % (W, chunk, case[:5]))
+
+
+APPEND_CASES = [
+    (4, 32, 8, 128, 1200, [1200, 1, 32, 33]),
+    (3, 64, 8, 64, 700, [700, 257, 2]),
+    (2, 16, 16, 128, 300, [300, 128]),  # r = 1
+    (2, 24, 1, 128, 500, [500, 17]),    # r = 24
+]
+
+
+@pytest.mark.parametrize("case", APPEND_CASES, ids=["d128_r4", "d64_r8", "d128_r1", "d128_r24"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("plan", ["default", "valu", "split128", "mergekernel"])
+def test_append_parity(env, case, dtype, plan):
+    """The new key/value land in row len-1 of the caches (bit-exact, nothing
+    else written) and the output matches the oracle's append-then-attend."""
+    B, H, G, d, L, lens = case
+    env(GQA_KERNEL="valu" if plan == "valu" else None, GQA_CHUNK=128 if plan in ("split128", "mergekernel") else None,
+        GQA_MERGE="kernel" if plan == "mergekernel" else None)
+    q, k, v, lens_t, scale = rand_case(B, H, G, d, L, lens, dtype, seed=61 + d + B)
+    gen = torch.Generator(DEV).manual_seed(99)
+    kn = torch.randn((B, G, d), generator=gen, device=DEV).to(k.dtype)
+    vn = torch.randn((B, G, d), generator=gen, device=DEV).to(k.dtype)
+    for W in (0, 100):
+        kc, vc = k.clone(), v.clone()
+        out = gqa.decode_append(q, kn, vn, kc, vc, lens_t, scale, window=W)
+        torch.cuda.synchronize()
+        ref, rk, rv = oracle.decode_append(q.cpu(), kn.cpu(), vn.cpu(), k.cpu(), v.cpu(), lens_t.cpu(), scale, window=W)
+        check(out, ref, dtype, "append window=%d %s %s" % (W, plan, case[:5]))
+        bits = torch.int16 if dtype == "bf16" else torch.int32
+        # NaN padding compares by bit pattern
+        assert np.array_equal(kc.cpu().view(bits).numpy().view(rk.dtype if dtype == "bf16" else np.int32),
+                              rk.view(np.uint16) if dtype == "bf16" else rk.view(np.int32))
+        assert np.array_equal(vc.cpu().view(bits).numpy().view(rv.dtype if dtype == "bf16" else np.int32),
+                              rv.view(np.uint16) if dtype == "bf16" else rv.view(np.int32))
+
+
+def test_append_matches_decode_of_updated_cache(env):
+    """Append-then-attend in one launch equals a plain decode of the updated
+    caches, bit for bit (same kernel arithmetic)."""
+    q, k, v, lens, scale = rand_case(16, 32, 8, 128, 4096, [4096] * 8 + [4000 - 301 * i for i in range(8)], "bf16",
+                                     seed=71)
+    gen = torch.Generator(DEV).manual_seed(7)
+    kn = torch.randn((16, 8, 128), generator=gen, device=DEV).to(torch.bfloat16)
+    vn = torch.randn((16, 8, 128), generator=gen, device=DEV).to(torch.bfloat16)
+    out_a = gqa.decode_append(q, kn, vn, k, v, lens, scale)
+    out_d = gqa.decode(q, k, v, lens, scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out_a, out_d)
+
+
 # --------------------------------------------------------------- the named workloads at full size
 
 FULL = [wl.MISTRAL_7B, wl.GEMMA2_27B] + [wl.t5xxl_sweep(g) for g in wl.T5XXL_SWEEP_G]
