@@ -195,6 +195,61 @@ def run_bench(args):
     print(json.dumps(line), flush=True)
 
 
+def fig6(args):
+    """The group sweep of the pages' Fig. 6 setup (input 2048, output 512) as
+    decoder attention on one GPU, per layer: for each of 512 output steps, a
+    self-attention decode with the cache append over the growing decoder cache
+    (lengths 1 .. 512) and a cross-attention decode over the 2048 encoder
+    positions.  T5-XXL shape: H = 64 heads of d = 64; G swept; B sequences.
+    Prints one JSON line per G (GPU time from HIP events on the launch stream)."""
+    import torch
+    import grouped_query_kv_decode_amd as gqa
+    from grouped_query_kv_decode_amd import workloads as wl
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B, H, d, T_in, T_out = args.fig6_batch, 64, 64, 2048, 512
+    for G in wl.T5XXL_SWEEP_G:
+        self_w = wl.Workload("fig6_self_G%d" % G, B, H, G, d, T_out, "bf16", 2000 + G, value_scale=0.5)
+        cross_w = wl.Workload("fig6_cross_G%d" % G, B, H, G, d, T_in, "bf16", 3000 + G, value_scale=0.5)
+        q, ks, vs, _ = wl.make_inputs(self_w, dev, pad="zero", seq_lens=torch.zeros(B, dtype=torch.int32))
+        _, kx, vx, lx = wl.make_inputs(cross_w, dev, pad="none")
+        gen = torch.Generator(dev).manual_seed(4000 + G)
+        k_new = (torch.randn((T_out, B, G, d), generator=gen, device=dev) * 0.5).to(torch.bfloat16)
+        v_new = (torch.randn((T_out, B, G, d), generator=gen, device=dev) * 0.5).to(torch.bfloat16)
+        lens = [torch.full((B,), t + 1, dtype=torch.int32, device=dev) for t in range(T_out)]
+        self_dec = [gqa.Decoder(q, ks, vs, lens[t], self_w.scale, k_new=k_new[t], v_new=v_new[t])
+                    for t in range(T_out)]
+        cross_dec = gqa.Decoder(q, kx, vx, lx, cross_w.scale)
+        for t in range(8):
+            self_dec[t]()
+            cross_dec()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for t in range(T_out):
+            self_dec[t]()
+            cross_dec()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        gpu_s = e0.elapsed_time(e1) * 1e-3
+        e = 2
+        self_bytes = sum(2 * G * (t + 1) * d * e for t in range(T_out)) * B + T_out * 2 * B * G * d * e
+        cross_bytes = T_out * 2 * G * T_in * d * e * B
+        qo_bytes = T_out * 2 * (2 * B * H * d * e)
+        ab = self_bytes + cross_bytes + qo_bytes
+        print(json.dumps({
+            "mode": "fig6", "G": G, "B": B, "H": H, "d": d, "input_len": T_in, "output_len": T_out,
+            "gpu_s_per_layer": gpu_s, "wall_s_per_layer": wall, "ms_per_output_step": gpu_s * 1e3 / T_out,
+            "tokens_per_s": B * T_out / gpu_s, "alg_GBps": ab / gpu_s / 1e9, "frac_of_8TBps": ab / gpu_s / 8e12,
+            "note": "attention only, one decoder layer; the pages' fig. 6 times whole T5-XXL inference per sample",
+        }), flush=True)
+        del q, ks, vs, kx, vx, k_new, v_new, self_dec, cross_dec
+        torch.cuda.empty_cache()
+
+
 def calibrate_copy(args):
     """A plain device-to-device copy of a known size (for counter scaling)."""
     import torch
@@ -282,6 +337,8 @@ def main():
     ap.add_argument("--window", type=int, default=4096, help="window for --variant window/append (0: none)")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time to aim for")
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--fig6", action="store_true", help="the pages' fig. 6 group sweep as decoder attention")
+    ap.add_argument("--fig6-batch", type=int, default=32)
     ap.add_argument("--summarize-rocprof", metavar="DIR")
     ap.add_argument("--write-traffic", action="store_true",
                     help="combine counter runs (--fetch-dir, --write-dir, --copy-fetch-dir, --copy-write-dir)")
@@ -303,6 +360,9 @@ def main():
         return 2
     if args.calibrate_copy:
         calibrate_copy(args)
+        return 0
+    if args.fig6:
+        fig6(args)
         return 0
     run_bench(args)
     return 0

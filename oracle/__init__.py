@@ -61,6 +61,10 @@ class Oracle:
             ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
             ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_void_p, ctypes.c_int,
         ]
+        lib.gqa_oracle_matmul.restype = ctypes.c_int
+        lib.gqa_oracle_matmul.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+        ]
         lib.gqa_oracle_meanpool.restype = ctypes.c_int
         lib.gqa_oracle_meanpool.argtypes = [
             ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
@@ -126,6 +130,40 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle decode_append rejected its arguments (rc=%d)" % rc)
         return out, ka, va
+
+    def matmul(self, x, w) -> np.ndarray:
+        """y[M,N] float64 = x[M,K] @ w[K,N] (same element type; bfloat16 exactly widened)."""
+        xa, ex = _host_array(x)
+        wa, ew = _host_array(w)
+        if ex != ew or xa.ndim != 2 or wa.ndim != 2 or xa.shape[1] != wa.shape[0]:
+            raise ValueError("expected x[M,K] and w[K,N] of one element type")
+        M, K = xa.shape
+        N = wa.shape[1]
+        y = np.empty((M, N), dtype=np.float64)
+        rc = self._lib.gqa_oracle_matmul(xa.ctypes.data, wa.ctypes.data, ex, M, K, N, y.ctypes.data)
+        if rc != 0:
+            raise ValueError("oracle matmul rejected its arguments (rc=%d)" % rc)
+        return y
+
+    def decode_layer(self, x, w_qkv, w_o, k_cache, v_cache, seq_lens, H: int, G: int, scale: float, window: int = 0):
+        """One decode step of the Implementation sketch's decode-step block for a
+        batch of tokens, in the storage type of its inputs (bfloat16 or binary32):
+        qkv = x @ w_qkv (columns: H query heads, then G key heads, then G value
+        heads, d each), rounded to the storage type; the new key/value appended
+        at position len-1; attention; the attention output rounded to the
+        storage type; y = out @ w_o.  Returns (y float64 [M, d_model], caches)."""
+        import torch
+        is_bf16 = isinstance(x, torch.Tensor) and x.dtype == torch.bfloat16
+        dt = torch.bfloat16 if is_bf16 else torch.float32
+        M = x.shape[0]
+        d = w_qkv.shape[1] // (H + 2 * G)
+        qkv = torch.from_numpy(self.matmul(x, w_qkv)).to(dt)
+        q = qkv[:, :H * d].reshape(M, H, d).contiguous()
+        kn = qkv[:, H * d:(H + G) * d].reshape(M, G, d).contiguous()
+        vn = qkv[:, (H + G) * d:].reshape(M, G, d).contiguous()
+        out, kc, vc = self.decode_append(q, kn, vn, k_cache, v_cache, seq_lens, scale, window=window)
+        att = torch.from_numpy(out).to(dt).reshape(M, H * d).contiguous()
+        return self.matmul(att, w_o), kc, vc, (q, kn, vn, att)
 
     def meanpool(self, w, H: int, G: int) -> np.ndarray:
         """w_out[d_model, G*h] float32 from w[d_model, H*h] float32."""
@@ -199,3 +237,11 @@ def decode_append(q, k_new, v_new, k_cache, v_cache, seq_lens, scale, nthreads=N
 
 def meanpool(w, H, G):
     return get().meanpool(w, H, G)
+
+
+def matmul(x, w):
+    return get().matmul(x, w)
+
+
+def decode_layer(x, w_qkv, w_o, k_cache, v_cache, seq_lens, H, G, scale, window=0):
+    return get().decode_layer(x, w_qkv, w_o, k_cache, v_cache, seq_lens, H, G, scale, window)

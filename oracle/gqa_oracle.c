@@ -188,6 +188,24 @@ int gqa_oracle_decode_append(const void *q, const void *k_new, const void *v_new
 }
 
 /*
+ * y[M,N] (binary64) = x[M,K] @ W[K,N]: the projections of the decode-step
+ * block (q = x @ Wq, key = x @ Wk, val = x @ Wv, and y = out @ Wo), one row
+ * of x per token.  x and W are stored as `elem`, row-major; the sum over k is
+ * taken in ascending order.  Returns 0, or -1 on a shape error.
+ */
+int gqa_oracle_matmul(const void *x, const void *w, int elem, int M, int K, int N, double *y) {
+  if (M < 0 || K <= 0 || N <= 0 || elem < ORACLE_F32 || elem > ORACLE_F64) return -1;
+  for (int m = 0; m < M; ++m)
+    for (int n = 0; n < N; ++n) {
+      double acc = 0.0;
+      for (int k = 0; k < K; ++k)
+        acc += widen(x, (size_t)m * K + k, elem) * widen(w, (size_t)k * N + n, elem);
+      y[(size_t)m * N + n] = acc;
+    }
+  return 0;
+}
+
+/*
  * Grouped mean-pool of a projection matrix w[d_model, H*h] (binary32, head i
  * owns columns i*h .. (i+1)*h-1) into w_out[d_model, G*h]: column block g is
  * the mean of the column blocks of heads g*r .. g*r+r-1, r = H/G.

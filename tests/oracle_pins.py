@@ -320,12 +320,54 @@ def pin_append_matches_sdpa(o):
             assert np.array_equal(out[2, h], vn[2, h // 4])
 
 
+def pin_matmul_numpy(o):
+    """The projections x @ W against numpy's matmul in float64; an identity W
+    returns x; rows and columns are not swapped (non-square shapes)."""
+    rng = np.random.default_rng(45)
+    for M, K, N in ((1, 8, 5), (3, 16, 24), (7, 5, 3)):
+        x = rng.standard_normal((M, K))
+        w = rng.standard_normal((K, N))
+        np.testing.assert_allclose(o.matmul(x, w), x @ w, rtol=0, atol=1e-12)
+    x = rng.standard_normal((4, 6))
+    assert np.array_equal(o.matmul(x, np.eye(6)), x)
+
+
+def pin_decode_layer_composition(o):
+    """The decode step with projections (batch, one token per sequence) equals
+    its stages: library matmuls for the projections, masked library SDPA over
+    the appended cache for attention."""
+    import torch
+    rng = np.random.default_rng(46)
+    B, H, G, d, L, dm = 3, 8, 2, 8, 9, 16
+    x = torch.from_numpy(rng.standard_normal((B, dm)))
+    wqkv = torch.from_numpy(rng.standard_normal((dm, (H + 2 * G) * d)) / 4)
+    wo = torch.from_numpy(rng.standard_normal((H * d, dm)) / 8)
+    _, k, v, lens, sc = _rand_case(rng, B, H, G, d, L, lens=[9, 4, 1])
+    y, kc, vc, _ = o.decode_layer(x.float(), wqkv.float(), wo.float(), k.astype(np.float32), v.astype(np.float32),
+                                  lens, H, G, sc)
+    qkv = (x.float().double() @ wqkv.float().double()).float().numpy().astype(np.float64)
+    q = qkv[:, :H * d].reshape(B, H, d)
+    kn = qkv[:, H * d:(H + G) * d].reshape(B, G, d)
+    vn = qkv[:, (H + G) * d:].reshape(B, G, d)
+    att = np.zeros((B, H, d))
+    for b in range(B):
+        n = int(lens[b])
+        kk = k[b].astype(np.float32).astype(np.float64)
+        vv = v[b].astype(np.float32).astype(np.float64)
+        kk[:, n - 1] = kn[b]
+        vv[:, n - 1] = vn[b]
+        att[b] = _sdpa_masked(q[b], kk, vv, sc, 0, n)
+    ref = att.astype(np.float32).astype(np.float64).reshape(B, H * d) @ wo.float().double().numpy()
+    np.testing.assert_allclose(y, ref, rtol=1e-6, atol=1e-6)
+
+
 DECODE_PINS = [
     pin_sdpa_enable_gqa, pin_sdpa_replicated_heads, pin_mha_endpoint, pin_mqa_endpoint,
     pin_weights_are_softmax, pin_large_scores, pin_constant_values, pin_single_position,
     pin_zero_query, pin_permutation_invariance, pin_padding_never_read, pin_equal_queries,
     pin_empty_and_clamped_lengths, pin_golden_decode, pin_bf16_and_f32_storage,
     pin_window_sdpa_mask, pin_window_closed_forms, pin_append_updates_the_cache, pin_append_matches_sdpa,
+    pin_matmul_numpy, pin_decode_layer_composition,
 ]
 
 

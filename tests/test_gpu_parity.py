@@ -320,6 +320,32 @@ def test_append_matches_decode_of_updated_cache(env):
     assert torch.equal(out_a, out_d)
 
 
+@pytest.mark.parametrize("G", [1, 8, 64])
+def test_encoder_decoder_steps(env, G):
+    """A few steps of the fig. 6 setup at small size: self-attention with the
+    cache append over a growing decoder cache, then cross-attention over the
+    encoder positions; every step against the oracle, cache included."""
+    B, H, d, T_in, T_out = 3, 64, 64, 300, 40
+    q, ks, vs, _, sc = rand_case(B, H, G, d, T_out, [T_out] * B, "bf16", seed=80 + G)
+    _, kx, vx, lx, _ = rand_case(B, H, G, d, T_in, [T_in, 250, 7], "bf16", seed=90 + G)
+    gen = torch.Generator(DEV).manual_seed(G)
+    ks_ref = ks.cpu()
+    vs_ref = vs.cpu()
+    for t in range(T_out):
+        kn = torch.randn((B, G, d), generator=gen, device=DEV).to(torch.bfloat16)
+        vn = torch.randn((B, G, d), generator=gen, device=DEV).to(torch.bfloat16)
+        lens = torch.full((B,), t + 1, dtype=torch.int32, device=DEV)
+        o_self = gqa.decode_append(q, kn, vn, ks, vs, lens, sc)
+        o_cross = gqa.decode(q, kx, vx, lx, sc)
+        torch.cuda.synchronize()
+        if t in (0, 1, 31, 32, T_out - 1):
+            ref, ks_ref_np, vs_ref_np = oracle.decode_append(q.cpu(), kn.cpu(), vn.cpu(), ks_ref, vs_ref, lens.cpu(), sc)
+            check(o_self, ref, "bf16", "self step %d G=%d" % (t, G))
+            check(o_cross, oracle.decode(q.cpu(), kx.cpu(), vx.cpu(), lx.cpu(), sc), "bf16", "cross G=%d" % G)
+        ks_ref = ks.cpu()
+        vs_ref = vs.cpu()
+
+
 # --------------------------------------------------------------- the named workloads at full size
 
 FULL = [wl.MISTRAL_7B, wl.GEMMA2_27B] + [wl.t5xxl_sweep(g) for g in wl.T5XXL_SWEEP_G]

@@ -28,6 +28,8 @@ MUTANTS = [
     ("append_wrong_row", "(size_t)Lmax + (size_t)(n - 1)) * d;", "(size_t)Lmax + (size_t)(n > 1 ? n - 2 : 0)) * d;"),
     ("append_value_from_key", "(const char *)v_new + src * es", "(const char *)k_new + src * es"),
     ("append_skipped", "memcpy((char *)k_cache + dst * es", "if (0) memcpy((char *)k_cache + dst * es"),
+    ("matmul_transposed_w", "widen(w, (size_t)k * N + n, elem)", "widen(w, (size_t)n * K + k, elem)"),
+    ("matmul_drops_last_k", "for (int k = 0; k < K; ++k)\n        acc +=", "for (int k = 0; k < K - 1; ++k)\n        acc +="),
     ("pool_divides_by_G", "(float)(acc / (double)r)", "(float)(acc / (double)G)"),
     ("pool_interleaved_columns", "acc += (double)wr[(size_t)i * h + c];", "acc += (double)wr[(size_t)c * H + i];"),
     ("pool_float_accumulator", "double acc = (double)wr[(size_t)(g * r) * h + c];",
