@@ -50,8 +50,16 @@ def alg_bytes(w, seq_lens, variant: str = "decode", window: int = 0) -> int:
     if window > 0:
         lens = lens.clamp(max=window)
     n = int(lens.sum())
+    kv = 2 * w.G * n * w.d * e
+    if variant == "layer":
+        # weights read once; x read, q/key/val and the attention output written
+        # and read back, y written; the cache rows of the new token written
+        dm, nqkv = w.d_model, (w.H + 2 * w.G) * w.d
+        weights = (dm * nqkv + w.H * w.d * dm) * e
+        acts = w.B * (dm + 2 * nqkv + 2 * w.H * w.d + dm) * e
+        return kv + weights + acts + 2 * w.B * w.G * w.d * e
     extra = 2 * w.B * w.G * w.d * e if variant == "append" else 0
-    return 2 * w.G * n * w.d * e + 2 * w.B * w.H * w.d * e + extra
+    return kv + 2 * w.B * w.H * w.d * e + extra
 
 
 def load_traffic(workload_name: str):
@@ -121,7 +129,14 @@ def run_bench(args):
     sets, decs = [], []
     for i in range(rot):
         q, k, v, lens = wl.make_inputs(w, dev, pad="none", seed_offset=i)
-        if args.variant == "append":
+        if args.variant == "layer":
+            gen = torch.Generator(dev).manual_seed(w.seed + 7 * i)
+            dm, nqkv = w.d_model, (w.H + 2 * w.G) * w.d
+            x = torch.randn((w.B, dm), generator=gen, device=dev).to(k.dtype)
+            w_qkv = (torch.randn((dm, nqkv), generator=gen, device=dev) * dm ** -0.5).to(k.dtype)
+            w_o = (torch.randn((w.H * w.d, dm), generator=gen, device=dev) * (w.H * w.d) ** -0.5).to(k.dtype)
+            dec = gqa.LayerStep(x, w_qkv, w_o, k, v, lens, w.H, w.G, w.scale)
+        elif args.variant == "append":
             gen = torch.Generator(dev).manual_seed(w.seed + 7 * i)
             kn = torch.randn((w.B, w.G, w.d), generator=gen, device=dev).to(k.dtype)
             vn = torch.randn((w.B, w.G, w.d), generator=gen, device=dev).to(k.dtype)
@@ -155,6 +170,8 @@ def run_bench(args):
     code = gqa.GQA_F32 if w.dtype == "f32" else gqa.GQA_BF16
     split = gqa.decode_workspace_size(w.B, w.H, w.G, w.d, w.Lmax, code) > 0
     kernels_per_step = 2 if split and os.environ.get("GQA_MERGE") == "kernel" else 1
+    if args.variant == "layer":
+        kernels_per_step += 2
     ab = alg_bytes(w, sets[0][3], args.variant, window)  # every rotation set has the same lengths
     achieved = ab / (avg_kernel_ms * 1e-3) / 1e9
     ms_per_step = wall * 1e3 / K
@@ -332,8 +349,9 @@ def main():
     ap.add_argument("--workload", default="mistral7b_bf16_B16_H32_G8_d128_L4096")
     ap.add_argument("--rotate", type=int, default=0, help="input sets cycled through (default: >= 1 GiB of caches)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--variant", choices=["decode", "append", "window"], default="decode",
-                    help="decode (default), decode with the cache append, or sliding-window decode")
+    ap.add_argument("--variant", choices=["decode", "append", "window", "layer"], default="decode",
+                    help="decode (default), decode with the cache append, sliding-window decode, or the whole "
+                         "decode step of a layer (q/k/v projection, append + attention, output projection)")
     ap.add_argument("--window", type=int, default=4096, help="window for --variant window/append (0: none)")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time to aim for")
     ap.add_argument("--calibrate-copy", action="store_true")

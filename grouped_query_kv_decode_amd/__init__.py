@@ -12,6 +12,8 @@ Entry points (same names as the C ABI, without the ``gqa_`` prefix):
     decode_window(q, k_cache, v_cache, seq_lens, scale, window, ...)
     decode_append(q, k_new, v_new, k_cache, v_cache, seq_lens, scale, window=0, ...)
     workspace_init(workspace)
+    linear(x, w, out=None, workspace=None)              y = x @ w (bfloat16 projections)
+    decode_layer(x, w_qkv, w_o, k_cache, v_cache, seq_lens, H, G, scale, window=0)
     meanpool_kv(w, H, G, out=None)
     decode_kernel_kind(B, H, G, d, Lmax, dtype)
 """
@@ -22,6 +24,7 @@ import os
 
 __all__ = [
     "GQAError", "decode", "decode_phase", "decode_window", "decode_append", "decode_workspace_size", "workspace_init", "meanpool_kv",
+    "linear", "linear_workspace_size", "decode_layer", "decode_layer_workspace_size", "LayerStep",
     "decode_kernel_kind", "status_string", "library_path", "load_library", "Decoder",
     "GQA_F32", "GQA_BF16",
 ]
@@ -36,7 +39,8 @@ STATUS_NAMES = {
 }
 EXPORTED = [
     "gqa_decode_workspace_size", "gqa_workspace_init", "gqa_decode", "gqa_decode_phase", "gqa_decode_window",
-    "gqa_decode_append", "gqa_meanpool_kv",
+    "gqa_decode_append", "gqa_linear_workspace_size", "gqa_linear", "gqa_decode_layer_workspace_size",
+    "gqa_decode_layer", "gqa_meanpool_kv",
     "gqa_status_string", "gqa_last_hip_error", "gqa_decode_kernel_kind",
 ]
 
@@ -79,6 +83,15 @@ def load_library(path: str | None = None):
     lib.gqa_decode_append.restype = ci
     lib.gqa_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ctypes.c_float, ci, vp, vp, sz,
                                       vp]
+    lib.gqa_linear_workspace_size.restype = sz
+    lib.gqa_linear_workspace_size.argtypes = [ci, ci, ci, ci]
+    lib.gqa_linear.restype = ci
+    lib.gqa_linear.argtypes = [vp, vp, vp, ci, ci, ci, ci, vp, sz, vp]
+    lib.gqa_decode_layer_workspace_size.restype = sz
+    lib.gqa_decode_layer_workspace_size.argtypes = [ci, ci, ci, ci, ci, ci, ci, ci]
+    lib.gqa_decode_layer.restype = ci
+    lib.gqa_decode_layer.argtypes = [vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, ctypes.c_float, ci, vp, vp,
+                                     sz, vp]
     lib.gqa_meanpool_kv.restype = ci
     lib.gqa_meanpool_kv.argtypes = [vp, ci, ci, ci, ci, vp, vp]
     lib.gqa_status_string.restype = ctypes.c_char_p
@@ -267,6 +280,96 @@ class Decoder:
         if st:
             raise GQAError(st, "gqa_decode_phase")
         return self.out
+
+
+def linear_workspace_size(M, K, N, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
+    return int(load_library().gqa_linear_workspace_size(M, K, N, code))
+
+
+def _check_dev(name, t, ref, shape, dtype):
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous() or t.device != ref.device \
+            or t.device.type != "cuda":
+        raise ValueError("%s must be a contiguous %s %s tensor on %s" % (name, list(shape), dtype, ref.device))
+
+
+def _ws_args(need, device, workspace):
+    if workspace is None and need > 0:
+        workspace = _workspace_for(need, device)
+    if workspace is None:
+        return None, 0, None
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size(), workspace
+
+
+def linear(x, w, out=None, workspace=None):
+    """y[M,N] = x[M,K] @ w[K,N] in bfloat16 (binary32 sums, rounded once)."""
+    import torch
+    M, K = x.shape
+    N = w.shape[1]
+    _check_dev("x", x, x, (M, K), torch.bfloat16)
+    _check_dev("w", w, x, (K, N), torch.bfloat16)
+    if out is None:
+        out = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    _check_dev("out", out, x, (M, N), torch.bfloat16)
+    ws_ptr, ws_bytes, _ = _ws_args(linear_workspace_size(M, K, N, GQA_BF16), x.device, workspace)
+    st = load_library().gqa_linear(x.data_ptr(), w.data_ptr(), out.data_ptr(), M, K, N, GQA_BF16, ws_ptr, ws_bytes,
+                                   _stream_handle(x.device))
+    if st:
+        raise GQAError(st, "gqa_linear")
+    return out
+
+
+def decode_layer_workspace_size(B, H, G, d, Lmax, window, d_model, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
+    return int(load_library().gqa_decode_layer_workspace_size(B, H, G, d, Lmax, window, d_model, code))
+
+
+class LayerStep:
+    """The full decode step (projections, cache append, attention, output
+    projection; gqa_decode_layer) bound to fixed tensors and to the stream
+    current at construction."""
+
+    def __init__(self, x, w_qkv, w_o, k_cache, v_cache, seq_lens, H: int, G: int, scale: float, window: int = 0,
+                 out=None, workspace=None):
+        import torch
+        B, d_model = x.shape
+        Bk, Gk, Lmax, d = k_cache.shape
+        if Bk != B or Gk != G or H % G:
+            raise ValueError("shape mismatch: x %s, k_cache %s, H=%d, G=%d" % (tuple(x.shape), tuple(k_cache.shape),
+                                                                               H, G))
+        bf = torch.bfloat16
+        _check_dev("x", x, x, (B, d_model), bf)
+        _check_dev("w_qkv", w_qkv, x, (d_model, (H + 2 * G) * d), bf)
+        _check_dev("w_o", w_o, x, (H * d, d_model), bf)
+        _check_dev("k_cache", k_cache, x, (B, G, Lmax, d), bf)
+        _check_dev("v_cache", v_cache, x, (B, G, Lmax, d), bf)
+        _check_dev("seq_lens", seq_lens, x, (B,), torch.int32)
+        if out is None:
+            out = torch.empty((B, d_model), dtype=bf, device=x.device)
+        _check_dev("out", out, x, (B, d_model), bf)
+        need = decode_layer_workspace_size(B, H, G, d, Lmax, int(window), d_model, GQA_BF16)
+        if need == 0 and B > 0:
+            raise GQAError(3, "gqa_decode_layer_workspace_size")
+        ws_ptr, ws_bytes, self.workspace = _ws_args(need, x.device, workspace)
+        self.out = out
+        self._keep = (x, w_qkv, w_o, k_cache, v_cache, seq_lens)
+        self._fn = load_library().gqa_decode_layer
+        self._args = (x.data_ptr(), w_qkv.data_ptr(), w_o.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                      seq_lens.data_ptr(), B, H, G, d, Lmax, int(window), d_model, float(scale), GQA_BF16,
+                      out.data_ptr(), ws_ptr, ws_bytes, _stream_handle(x.device))
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st:
+            raise GQAError(st, "gqa_decode_layer")
+        return self.out
+
+
+def decode_layer(x, w_qkv, w_o, k_cache, v_cache, seq_lens, H: int, G: int, scale: float, window: int = 0,
+                 out=None, workspace=None):
+    """y[B, d_model] = one decode step of a GQA attention layer (see LayerStep);
+    the caches receive the new token's keys and values in place."""
+    return LayerStep(x, w_qkv, w_o, k_cache, v_cache, seq_lens, H, G, scale, window, out, workspace)()
 
 
 def meanpool_kv(w, H: int, G: int, out=None):

@@ -137,6 +137,99 @@ gqa_status make_plan(int B, int H, int G, int d, int Lmax, gqa_dtype dt, Plan *p
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// Projection plan: 128-column blocks x k splits; a split takes whole 32-row
+// steps.  k is split until the grid holds about 512 workgroups of 4 waves,
+// keeping at least two steps per wave.
+struct LinearPlan {
+  int KS, ksteps_per_split, NW;
+  unsigned grid;
+  size_t ws_bytes;  // counters + partials, 0 when k is not split
+};
+
+gqa_status check_linear(int M, int K, int N, gqa_dtype dt) {
+  if (dt != GQA_F32 && dt != GQA_BF16) return GQA_ERR_UNSUPPORTED;
+  if (M < 0 || K < 1 || N < 1) return GQA_ERR_SHAPE;
+  if (dt != GQA_BF16 || M > 64 || K % 32 != 0 || N % 128 != 0) return GQA_ERR_UNSUPPORTED;
+  return GQA_OK;
+}
+
+gqa_status make_linear_plan(int M, int K, int N, LinearPlan *pl) {
+  const int ntile = N / 128;
+  const int ksteps = K / 32;
+  pl->NW = 4;
+  int KS = env_int("GQA_LINEAR_KSPLIT", 0);
+  if (KS == 0) {
+    KS = (512 + ntile - 1) / ntile;
+    const int max_ks = ksteps / (2 * pl->NW);
+    if (KS > max_ks) KS = max_ks;
+    if (KS < 1) KS = 1;
+  }
+  if (KS > ksteps) KS = ksteps;
+  pl->ksteps_per_split = ceil_div(ksteps, KS);
+  pl->KS = ceil_div(ksteps, pl->ksteps_per_split);
+  const unsigned long long grid = (unsigned long long)ntile * pl->KS;
+  if (grid == 0 || grid > 0x7fffffffULL || ntile > kMaxFusedUnits) return GQA_ERR_SIZE;
+  pl->grid = (unsigned)grid;
+  pl->ws_bytes = pl->KS > 1 ? kCounterBytes + (size_t)pl->KS * M * N * sizeof(float) : 0;
+  return GQA_OK;
+}
+
+gqa_status linear_impl(const void *x, const void *w, void *const y[3], const int seg_lo[4], int nseg, int M, int K,
+                       int N, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  LinearPlan pl;
+  gqa_status st = make_linear_plan(M, K, N, &pl);
+  if (st != GQA_OK) return st;
+  if (pl.ws_bytes > 0) {
+    if (!workspace) return GQA_ERR_NULL;
+    if (workspace_bytes < pl.ws_bytes) return GQA_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return GQA_ERR_ALIGN;
+  }
+  gqa::LinearParams p;
+  p.x = static_cast<const __bf16 *>(x);
+  p.w = static_cast<const __bf16 *>(w);
+  for (int i = 0; i < 3; ++i) p.y[i] = static_cast<__bf16 *>(y[i]);
+  for (int i = 0; i < 4; ++i) p.seg_lo[i] = seg_lo[i];
+  p.nseg = nseg;
+  p.ws_cnt = pl.ws_bytes ? static_cast<unsigned *>(workspace) : nullptr;
+  p.ws_part = pl.ws_bytes ? reinterpret_cast<float *>(static_cast<char *>(workspace) + kCounterBytes) : nullptr;
+  p.M = M;
+  p.K = K;
+  p.N = N;
+  p.KS = pl.KS;
+  p.ksteps_per_split = pl.ksteps_per_split;
+  const hipError_t e = gqa::launch_linear(p, pl.NW, pl.grid, stream);
+  return e == hipSuccess ? GQA_OK : hip_fail(e);
+}
+
+// Workspace of the full decode step (gqa_decode_layer): one scratch region
+// (counters + partials) that the three kernels use in turn, then q, the new
+// keys and values, and the attention output.
+struct LayerPlan {
+  size_t scratch, q_off, kn_off, vn_off, att_off, total;
+};
+
+gqa_status make_layer_plan(int B, int H, int G, int d, int Lmax, int window, int d_model, LayerPlan *lp) {
+  Plan ap;
+  const int Leff = (window > 0 && window < Lmax) ? window : Lmax;
+  gqa_status st = make_plan(B, H, G, d, Leff, GQA_BF16, &ap);
+  if (st != GQA_OK) return st;
+  LinearPlan l1, l2;
+  st = make_linear_plan(B, d_model, (H + 2 * G) * d, &l1);
+  if (st != GQA_OK) return st;
+  st = make_linear_plan(B, H * d, d_model, &l2);
+  if (st != GQA_OK) return st;
+  size_t scratch = ap.ws_bytes;
+  if (l1.ws_bytes > scratch) scratch = l1.ws_bytes;
+  if (l2.ws_bytes > scratch) scratch = l2.ws_bytes;
+  lp->scratch = round_up(scratch, 256);
+  lp->q_off = lp->scratch;
+  lp->kn_off = lp->q_off + round_up((size_t)B * H * d * 2, 256);
+  lp->vn_off = lp->kn_off + round_up((size_t)B * G * d * 2, 256);
+  lp->att_off = lp->vn_off + round_up((size_t)B * G * d * 2, 256);
+  lp->total = lp->att_off + round_up((size_t)B * H * d * 2, 256);
+  return GQA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -271,6 +364,68 @@ gqa_status gqa_decode_append(const void *q, const void *k_new, const void *v_new
   if (B > 0 && (!k_new || !v_new)) return GQA_ERR_NULL;
   return decode_impl(0, q, k_new, v_new, k_cache, v_cache, seq_lens, B, H, G, d, Lmax, window, scale, dtype, out,
                      workspace, workspace_bytes, stream);
+}
+
+size_t gqa_linear_workspace_size(int M, int K, int N, gqa_dtype dtype) {
+  if (check_linear(M, K, N, dtype) != GQA_OK || M == 0) return 0;
+  LinearPlan pl;
+  return make_linear_plan(M, K, N, &pl) == GQA_OK ? pl.ws_bytes : 0;
+}
+
+gqa_status gqa_linear(const void *x, const void *w, void *y, int M, int K, int N, gqa_dtype dtype, void *workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+  const gqa_status st = check_linear(M, K, N, dtype);
+  if (st != GQA_OK) return st;
+  if (M == 0) return GQA_OK;
+  if (!x || !w || !y) return GQA_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y, 16)) return GQA_ERR_ALIGN;
+  void *ys[3] = {y, nullptr, nullptr};
+  const int seg[4] = {0, N, N, N};
+  return linear_impl(x, w, ys, seg, 1, M, K, N, workspace, workspace_bytes, stream);
+}
+
+size_t gqa_decode_layer_workspace_size(int B, int H, int G, int d, int Lmax, int window, int d_model,
+                                       gqa_dtype dtype) {
+  if (check_shape(B, H, G, d, Lmax, dtype) != GQA_OK || B == 0 || window < 0) return 0;
+  if (check_linear(B, d_model, (H + 2 * G) * d, dtype) != GQA_OK || check_linear(B, H * d, d_model, dtype) != GQA_OK)
+    return 0;
+  LayerPlan lp;
+  return make_layer_plan(B, H, G, d, Lmax, window, d_model, &lp) == GQA_OK ? lp.total : 0;
+}
+
+gqa_status gqa_decode_layer(const void *x, const void *w_qkv, const void *w_o, void *k_cache, void *v_cache,
+                            const int32_t *seq_lens, int B, int H, int G, int d, int Lmax, int window, int d_model,
+                            float scale, gqa_dtype dtype, void *y, void *workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+  gqa_status st = check_shape(B, H, G, d, Lmax, dtype);
+  if (st != GQA_OK) return st;
+  if (window < 0 || d_model < 1) return GQA_ERR_SHAPE;
+  st = check_linear(B, d_model, (H + 2 * G) * d, dtype);
+  if (st == GQA_OK) st = check_linear(B, H * d, d_model, dtype);
+  if (st != GQA_OK) return st;
+  if (B == 0) return GQA_OK;
+  if (!x || !w_qkv || !w_o || !k_cache || !v_cache || !seq_lens || !y || !workspace) return GQA_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(w_qkv, 16) || !aligned(w_o, 16) || !aligned(y, 16)) return GQA_ERR_ALIGN;
+  if (!aligned(workspace, 256)) return GQA_ERR_ALIGN;
+  LayerPlan lp;
+  st = make_layer_plan(B, H, G, d, Lmax, window, d_model, &lp);
+  if (st != GQA_OK) return st;
+  if (workspace_bytes < lp.total) return GQA_ERR_WORKSPACE;
+  char *ws = static_cast<char *>(workspace);
+  void *q = ws + lp.q_off, *kn = ws + lp.kn_off, *vn = ws + lp.vn_off, *att = ws + lp.att_off;
+  // 1. q, key, val = x @ [Wq | Wk | Wv], written as three tensors
+  void *ys[3] = {q, kn, vn};
+  const int seg[4] = {0, H * d, (H + G) * d, (H + 2 * G) * d};
+  st = linear_impl(x, w_qkv, ys, seg, 3, B, d_model, (H + 2 * G) * d, ws, lp.scratch, stream);
+  if (st != GQA_OK) return st;
+  // 2. append the new key/value to the caches, attend
+  st = decode_impl(0, q, kn, vn, k_cache, v_cache, seq_lens, B, H, G, d, Lmax, window, scale, dtype, att, ws,
+                   lp.scratch, stream);
+  if (st != GQA_OK) return st;
+  // 3. y = out @ Wo
+  void *yo[3] = {y, nullptr, nullptr};
+  const int seg_o[4] = {0, d_model, d_model, d_model};
+  return linear_impl(att, w_o, yo, seg_o, 1, B, H * d, d_model, ws, lp.scratch, stream);
 }
 
 gqa_status gqa_meanpool_kv(const float *w, int d_model, int H, int G, int h, float *w_out, hipStream_t stream) {

@@ -44,6 +44,11 @@ class Workload:
     def r(self) -> int:
         return self.H // self.G
 
+    @property
+    def d_model(self) -> int:
+        """Width of the token's hidden state for the projections: H * d."""
+        return self.H * self.d
+
     def with_(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
 

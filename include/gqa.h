@@ -160,6 +160,59 @@ gqa_status gqa_decode_append(const void *q, const void *k_new, const void *v_new
                              hipStream_t stream);
 
 /*
+ * Projection of the decode-step block (wikillm "Grouped-query attention
+ * (GQA)", Implementation sketch: q = x Wq, key = x Wk, val = x Wv, and the
+ * output projection Wo), for a batch of M tokens:
+ *   y[M, N] = x[M, K] @ w[K, N]
+ *   x  [M, K] bfloat16, row-major, device, 16-byte aligned; one row per token.
+ *   w  [K, N] bfloat16, row-major, device, 16-byte aligned (read once).
+ *   y  [M, N] bfloat16, device, 16-byte aligned; each element is the binary32
+ *      sum rounded once to bfloat16 (nearest even).
+ *   M in 0..64 (M = 0 is a no-op), K a multiple of 32, N a multiple of 128,
+ *   dtype GQA_BF16 (GQA_ERR_UNSUPPORTED otherwise; GQA_ERR_SHAPE for K or
+ *   N < 1 or M < 0).
+ *   workspace  gqa_linear_workspace_size(M, K, N, dtype) bytes (0: may be
+ *      NULL), cleared once with gqa_workspace_init, 256-byte aligned; when K is
+ *      split across workgroups it holds arrival counters (left at zero after
+ *      each call) and binary32 partial sums, added in a fixed order, so
+ *      results are deterministic.  Calls that share a workspace must be
+ *      ordered (one stream).
+ * Status codes as for gqa_decode.
+ */
+size_t gqa_linear_workspace_size(int M, int K, int N, gqa_dtype dtype);
+gqa_status gqa_linear(const void *x, const void *w, void *y, int M, int K, int N, gqa_dtype dtype, void *workspace,
+                      size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The whole decode-step block of wikillm "Grouped-query attention (GQA)"
+ * (Implementation sketch) for B sequences, one new token each, enqueued as
+ * three kernels on `stream`:
+ *   1. [q | key | val] = x @ w_qkv           (gqa_linear, output split in three)
+ *   2. key/val appended at row len_b - 1 of the caches; out = attention
+ *      (gqa_decode_append, with `window` as there)
+ *   3. y = out @ w_o                           (gqa_linear)
+ *   x      [B, d_model] bfloat16, device: the token's hidden state.
+ *   w_qkv  [d_model, (H + 2G) d] bfloat16: columns H d of query heads, then G d
+ *          of key heads, then G d of value heads (head i owns d columns).
+ *   w_o    [H d, d_model] bfloat16.
+ *   k_cache, v_cache, seq_lens, B, H, G, d, Lmax, window, scale: as for
+ *          gqa_decode_append (caches updated in place).
+ *   y      [B, d_model] bfloat16.
+ * q, key, val and out are rounded to bfloat16 between the steps (they live in
+ * the workspace).  dtype must be GQA_BF16, B <= 64, d_model and (H + 2G) d
+ * multiples of 128, H d a multiple of 32 (GQA_ERR_UNSUPPORTED otherwise).
+ * Other status codes as for gqa_decode.  Workspace:
+ * gqa_decode_layer_workspace_size(...) bytes, 256-byte aligned, cleared once
+ * with gqa_workspace_init.
+ */
+size_t gqa_decode_layer_workspace_size(int B, int H, int G, int d, int Lmax, int window, int d_model,
+                                       gqa_dtype dtype);
+gqa_status gqa_decode_layer(const void *x, const void *w_qkv, const void *w_o, void *k_cache, void *v_cache,
+                            const int32_t *seq_lens, int B, int H, int G, int d, int Lmax, int window, int d_model,
+                            float scale, gqa_dtype dtype, void *y, void *workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+
+/*
  * The pages' checkpoint conversion step, numeric core only: wikillm
  * "Grouped-query attention (GQA)", Implementation sketch (conversion block)
  * and Variants ("Converted and uptrained checkpoints"): the key (or value)

@@ -162,6 +162,70 @@ def test_window_and_append_arguments(lib):
     assert app(kn=None, vn=None, B=0) == OK
 
 
+def _linear_ws(M, K, N):
+    """Workspace model of gqa_linear: 128-column blocks, k split in whole
+    32-row steps until about 512 workgroups (at least two steps per wave of 4)."""
+    ntile, ksteps = N // 128, K // 32
+    ks = max(1, min(-(-512 // ntile), ksteps // 8))
+    per = -(-ksteps // ks)
+    ks = -(-ksteps // per)
+    return 0 if ks == 1 else 256 * 1024 + ks * M * N * 4
+
+
+def test_linear_arguments(lib):
+    lin = lambda x=P, w=P, y=P, M=4, K=256, N=256, dt=BF16, ws=None, nb=0: lib.gqa_linear(x, w, y, M, K, N, dt, ws,
+                                                                                          nb, None)
+    assert lin(dt=F32) == UNSUP
+    assert lin(M=65) == UNSUP
+    assert lin(K=48) == UNSUP
+    assert lin(N=200) == UNSUP
+    assert lin(M=-1) == SHAPE
+    assert lin(K=0) == SHAPE
+    assert lin(N=0) == SHAPE
+    assert lin(M=0, x=None, w=None, y=None) == OK
+    assert lin(x=None) == NULL
+    assert lin(y=P + 2) == ALIGN
+    # k split (K = 4096 over 2 column blocks): the workspace is required
+    assert lin(M=4, K=4096, N=256, ws=None) == NULL
+    assert lin(M=4, K=4096, N=256, ws=P, nb=_linear_ws(4, 4096, 256) - 1) == WS
+    assert lin(M=4, K=4096, N=256, ws=P + 64, nb=1 << 30) == ALIGN
+
+
+def test_linear_workspace_model(lib):
+    for M, K, N in [(16, 4096, 6144), (16, 4096, 4096), (1, 256, 128), (64, 8192, 1024), (3, 64, 128 * 600),
+                    (8, 96, 128)]:
+        assert lib.gqa_linear_workspace_size(M, K, N, BF16) == _linear_ws(M, K, N), (M, K, N)
+    assert lib.gqa_linear_workspace_size(16, 4096, 4096, F32) == 0
+    assert lib.gqa_linear_workspace_size(0, 4096, 4096, BF16) == 0
+
+
+def test_decode_layer_arguments(lib):
+    # Mistral-7B shape: d_model 4096, H 32, G 8, d 128
+    need = lib.gqa_decode_layer_workspace_size(16, 32, 8, 128, 4096, 0, 4096, BF16)
+    att = lib.gqa_decode_workspace_size(16, 32, 8, 128, 4096, BF16)
+    scratch = max(att, _linear_ws(16, 4096, 6144), _linear_ws(16, 32 * 128, 4096))
+    bufs = 2 * (16 * 32 * 128) * 2 + 2 * (16 * 8 * 128) * 2
+    assert need == -(-scratch // 256) * 256 + bufs
+    assert lib.gqa_decode_layer_workspace_size(16, 32, 8, 128, 4096, 0, 4096, F32) == 0
+    assert lib.gqa_decode_layer_workspace_size(65, 32, 8, 128, 4096, 0, 4096, BF16) == 0
+    assert lib.gqa_decode_layer_workspace_size(16, 32, 8, 128, 4096, 0, 4000, BF16) == 0
+
+    def layer(x=P, w1=P, w2=P, B=2, H=8, G=2, d=128, W=0, dm=1024, dt=BF16, ws=P, nb=1 << 30):
+        return lib.gqa_decode_layer(x, w1, w2, P, P, P, B, H, G, d, 512, W, dm, 0.125, dt, P, ws, nb, None)
+    assert layer(dt=F32) == UNSUP
+    assert layer(B=65) == UNSUP
+    assert layer(dm=1000) == UNSUP
+    assert layer(H=7) == SHAPE
+    assert layer(W=-1) == SHAPE
+    assert layer(dm=0) == SHAPE
+    assert layer(B=0, x=None, ws=None) == OK
+    assert layer(x=None) == NULL
+    assert layer(ws=None) == NULL
+    assert layer(w2=P + 4) == ALIGN
+    assert layer(ws=P + 128) == ALIGN
+    assert layer(nb=lib.gqa_decode_layer_workspace_size(2, 8, 2, 128, 512, 0, 1024, BF16) - 1) == WS
+
+
 def test_binding_rejects_bad_tensors():
     import torch
     q = torch.zeros(2, 8, 64)
