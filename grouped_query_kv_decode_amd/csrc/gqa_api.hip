@@ -138,10 +138,13 @@ gqa_status make_plan(int B, int H, int G, int d, int Lmax, gqa_dtype dt, Plan *p
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 // Projection plan: 128-column blocks x k splits; a split takes whole 32-row
-// steps.  k is split until the grid holds about 512 workgroups of 4 waves,
-// keeping at least two steps per wave.
+// steps.  k is split in a power of two of parts, the largest that keeps the
+// grid within one workgroup of 4 waves per compute unit (256) and at least
+// two steps per wave: every split adds partial sums that the last workgroup
+// of the column block reads back, so more workgroups than compute units
+// cost more in that tail than they gain.
 struct LinearPlan {
-  int KS, ksteps_per_split, NW;
+  int KS, ksteps_per_split, NW, TPI;
   unsigned grid;
   size_t ws_bytes;  // counters + partials, 0 when k is not split
 };
@@ -156,17 +159,25 @@ gqa_status check_linear(int M, int K, int N, gqa_dtype dt) {
 gqa_status make_linear_plan(int M, int K, int N, LinearPlan *pl) {
   const int ntile = N / 128;
   const int ksteps = K / 32;
-  pl->NW = 4;
+  pl->NW = env_int("GQA_LINEAR_WAVES", 4) == 8 ? 8 : 4;
   int KS = env_int("GQA_LINEAR_KSPLIT", 0);
   if (KS == 0) {
-    KS = (512 + ntile - 1) / ntile;
     const int max_ks = ksteps / (2 * pl->NW);
-    if (KS > max_ks) KS = max_ks;
-    if (KS < 1) KS = 1;
+    KS = 1;
+    while (2 * KS * ntile <= 256 && 2 * KS <= max_ks) KS *= 2;
   }
   if (KS > ksteps) KS = ksteps;
   pl->ksteps_per_split = ceil_div(ksteps, KS);
   pl->KS = ceil_div(ksteps, pl->ksteps_per_split);
+  // steps loaded together: a wave's whole share when it fits the registers
+  const int per_wave = ceil_div(pl->ksteps_per_split, pl->NW);
+  const int tb = ceil_div(M, 16) > 2 ? 4 : ceil_div(M, 16);
+  const int max_tpi = tb == 4 ? 2 : 4;
+  pl->TPI = per_wave >= 3 ? 4 : per_wave;
+  if (pl->TPI < 1) pl->TPI = 1;
+  if (pl->TPI > max_tpi) pl->TPI = max_tpi;
+  const int tpi_env = env_int("GQA_LINEAR_TPI", 0);
+  if (tpi_env == 1 || tpi_env == 2 || (tpi_env == 4 && max_tpi == 4)) pl->TPI = tpi_env;
   const unsigned long long grid = (unsigned long long)ntile * pl->KS;
   if (grid == 0 || grid > 0x7fffffffULL || ntile > kMaxFusedUnits) return GQA_ERR_SIZE;
   pl->grid = (unsigned)grid;
@@ -197,7 +208,7 @@ gqa_status linear_impl(const void *x, const void *w, void *const y[3], const int
   p.N = N;
   p.KS = pl.KS;
   p.ksteps_per_split = pl.ksteps_per_split;
-  const hipError_t e = gqa::launch_linear(p, pl.NW, pl.grid, stream);
+  const hipError_t e = gqa::launch_linear(p, pl.NW, pl.TPI, pl.grid, stream);
   return e == hipSuccess ? GQA_OK : hip_fail(e);
 }
 

@@ -200,7 +200,7 @@ __device__ void merge_heads(const DecodeParams &p, int b, int head0, int nh, int
 hipError_t launch_decode_valu(const DecodeParams &p, int dtype, int D, int RC, unsigned grid, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeParams &p, int D, int HB, int NW, unsigned grid, hipStream_t stream);
 hipError_t launch_merge(const DecodeParams &p, int dtype, int D, int heads_per_unit, hipStream_t stream);
-hipError_t launch_linear(const LinearParams &p, int NW, unsigned grid, hipStream_t stream);
+hipError_t launch_linear(const LinearParams &p, int NW, int TPI, unsigned grid, hipStream_t stream);
 hipError_t launch_meanpool(const float *w, int d_model, int H, int G, int h, float *w_out, hipStream_t stream);
 hipError_t launch_fill_zero(void *ptr, size_t bytes, hipStream_t stream);
 

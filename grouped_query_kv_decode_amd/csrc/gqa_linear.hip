@@ -50,7 +50,10 @@ __device__ __forceinline__ __bf16 *out_ptr(const LinearParams &p, int row, int c
   return p.y[s] + (size_t)row * w + (col - p.seg_lo[s]);
 }
 
-template <int TB, int NW>
+// A wave's steps are kstep0 + wave + j*NW.  TPI steps are loaded before any
+// is used (one memory round trip for all of them); a step past the split's
+// end re-reads the split's last step (in bounds, from cache) and is skipped.
+template <int TB, int NW, int TPI>
 __global__ __launch_bounds__(64 * NW) void linear_mfma(LinearParams p) {
   constexpr int kCols = 128;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -70,46 +73,77 @@ __global__ __launch_bounds__(64 * NW) void linear_mfma(LinearParams p) {
     for (int db = 0; db < 8; ++db) acc[tb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const __bf16 *wl = p.w + (size_t)(8 * c) * p.N + col0 + 8 * nn;  // lane's first row / column
-  for (int st = kstep0 + wave; st < kstep1; st += NW) {
-    const int k = st * 32;
-    u32x4 wR[8];
-    const __bf16 *wk = wl + (size_t)k * p.N;
+  for (int base = kstep0 + wave; base < kstep1; base += TPI * NW) {
+    u32x4 wR[TPI][8];
+    u32x4 xB[TPI][TB];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) wR[u] = *reinterpret_cast<const u32x4 *>(wk + (size_t)u * p.N);
-    u32x4 xB[TB];
+    for (int j = 0; j < TPI; ++j) {
+      const int k = min(base + j * NW, kstep1 - 1) * 32;
+      const __bf16 *wk = wl + (size_t)k * p.N;
 #pragma unroll
-    for (int tb = 0; tb < TB; ++tb) {
-      const int row = tb * 16 + nn;
-      xB[tb] = row < p.M ? *reinterpret_cast<const u32x4 *>(p.x + (size_t)row * p.K + k + 8 * c)
-                         : u32x4{0u, 0u, 0u, 0u};
+      for (int u = 0; u < 8; ++u) wR[j][u] = *reinterpret_cast<const u32x4 *>(wk + (size_t)u * p.N);
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb) {
+        const int row = tb * 16 + nn;
+        xB[j][tb] = row < p.M ? *reinterpret_cast<const u32x4 *>(p.x + (size_t)row * p.K + k + 8 * c)
+                              : u32x4{0u, 0u, 0u, 0u};
+      }
     }
-#define GQA_LIN_STEP(DB)                                                              \
-  {                                                                                   \
-    const u32x4 a = column<DB>(wR);                                                   \
-    _Pragma("unroll") for (int tb = 0; tb < TB; ++tb) acc[tb][DB] = mfma(a, xB[tb], acc[tb][DB]); \
+#pragma unroll
+    for (int j = 0; j < TPI; ++j) {
+      if (base + j * NW >= kstep1) break;
+#define GQA_LIN_STEP(DB)                                                                           \
+  {                                                                                                \
+    const u32x4 a = column<DB>(wR[j]);                                                             \
+    _Pragma("unroll") for (int tb = 0; tb < TB; ++tb) acc[tb][DB] = mfma(a, xB[j][tb], acc[tb][DB]); \
   }
-    GQA_LIN_STEP(0) GQA_LIN_STEP(1) GQA_LIN_STEP(2) GQA_LIN_STEP(3)
-    GQA_LIN_STEP(4) GQA_LIN_STEP(5) GQA_LIN_STEP(6) GQA_LIN_STEP(7)
+      GQA_LIN_STEP(0) GQA_LIN_STEP(1) GQA_LIN_STEP(2) GQA_LIN_STEP(3)
+      GQA_LIN_STEP(4) GQA_LIN_STEP(5) GQA_LIN_STEP(6) GQA_LIN_STEP(7)
 #undef GQA_LIN_STEP
+    }
   }
 
-  // Sum the waves in wave order through LDS: sm[token][column].
+  // Sum the waves in wave order through LDS into sm[token][column].  When
+  // every wave's accumulator fits, all waves write their own slice and the
+  // sum is read back in parallel after one barrier; otherwise the waves add
+  // into one slice in turn.
   constexpr int LD = kCols + 4;
-  __shared__ float sm[TB * 16 * LD];
-  for (int w = 0; w < NW; ++w) {
-    if (wave == w) {
+  constexpr bool kSlices = NW * TB * 16 * LD * 4 <= 64 * 1024;
+  __shared__ float sm[(kSlices ? NW : 1) * TB * 16 * LD];
+  if constexpr (kSlices) {
+    float *mine = sm + wave * (TB * 16 * LD);
 #pragma unroll
-      for (int tb = 0; tb < TB; ++tb)
+    for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int db = 0; db < 8; ++db) {
-            float *e = sm + (tb * 16 + nn) * LD + 8 * (4 * c + i) + db;
-            *e = w == 0 ? acc[tb][db][i] : *e + acc[tb][db][i];
-          }
-    }
+        for (int db = 0; db < 8; ++db) mine[(tb * 16 + nn) * LD + 8 * (4 * c + i) + db] = acc[tb][db][i];
     __syncthreads();
+  } else {
+    for (int w = 0; w < NW; ++w) {
+      if (wave == w) {
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int db = 0; db < 8; ++db) {
+              float *e = sm + (tb * 16 + nn) * LD + 8 * (4 * c + i) + db;
+              *e = w == 0 ? acc[tb][db][i] : *e + acc[tb][db][i];
+            }
+      }
+      __syncthreads();
+    }
   }
+  // total of element (row, col) over the waves, in wave order
+  auto total = [&](int row, int col) {
+    float t = sm[row * LD + col];
+    if constexpr (kSlices) {
+#pragma unroll
+      for (int w = 1; w < NW; ++w) t += sm[w * (TB * 16 * LD) + row * LD + col];
+    }
+    return t;
+  };
 
   // One k split: round and store.  Several: device-scope partials, and the
   // last workgroup of the column block sums them in split order.
@@ -117,46 +151,85 @@ __global__ __launch_bounds__(64 * NW) void linear_mfma(LinearParams p) {
   if (p.KS == 1) {
     for (int idx = threadIdx.x; idx < rows * kCols; idx += blockDim.x) {
       const int row = idx / kCols, col = idx % kCols;
-      *out_ptr(p, row, col0 + col) = (__bf16)sm[row * LD + col];
+      *out_ptr(p, row, col0 + col) = (__bf16)total(row, col);
     }
     return;
   }
   for (int idx = threadIdx.x * 4; idx < rows * kCols; idx += blockDim.x * 4) {
     const int row = idx / kCols, col = idx % kCols;
-    const float *e = sm + row * LD + col;
-    store_partial4(p.ws_part + ((size_t)ks * p.M + row) * p.N + col0 + col, e[0], e[1], e[2], e[3]);
+    store_partial4(p.ws_part + ((size_t)ks * p.M + row) * p.N + col0 + col, total(row, col), total(row, col + 1),
+                   total(row, col + 2), total(row, col + 3));
   }
   if (!arrive_last(p.ws_cnt + tile, p.KS)) return;
-  for (int idx = threadIdx.x * 2; idx < rows * kCols; idx += blockDim.x * 2) {
-    const int row = idx / kCols, col = idx % kCols;
-    float s0 = 0.f, s1 = 0.f;
-    for (int s = 0; s < p.KS; ++s) {
-      const float2 v = load_pair(p.ws_part + ((size_t)s * p.M + row) * p.N + col0 + col);
-      s0 += v.x;
-      s1 += v.y;
+  // Each thread sums kPairs column pairs; the loads of kBatch splits for all
+  // of them are issued before the adds.
+  constexpr int kPairs = 4, kBatch = 8;
+  const int npairs = rows * kCols / 2;
+  for (int base = threadIdx.x; base < npairs; base += blockDim.x * kPairs) {
+    float2 sum[kPairs];
+#pragma unroll
+    for (int i = 0; i < kPairs; ++i) sum[i] = make_float2(0.f, 0.f);
+    for (int s0 = 0; s0 < p.KS; s0 += kBatch) {
+      float2 v[kPairs][kBatch];
+#pragma unroll
+      for (int i = 0; i < kPairs; ++i) {
+        const int pr = base + i * blockDim.x;
+        const int row = (2 * pr) / kCols, col = (2 * pr) % kCols;
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u)
+          if (pr < npairs && s0 + u < p.KS)
+            v[i][u] = load_pair(p.ws_part + ((size_t)(s0 + u) * p.M + row) * p.N + col0 + col);
+      }
+#pragma unroll
+      for (int i = 0; i < kPairs; ++i)
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u)
+          if (s0 + u < p.KS) {
+            sum[i].x += v[i][u].x;
+            sum[i].y += v[i][u].y;
+          }
     }
-    *out_ptr(p, row, col0 + col) = (__bf16)s0;
-    *out_ptr(p, row, col0 + col + 1) = (__bf16)s1;
+#pragma unroll
+    for (int i = 0; i < kPairs; ++i) {
+      const int pr = base + i * blockDim.x;
+      if (pr < npairs) {
+        const int row = (2 * pr) / kCols, col = (2 * pr) % kCols;
+        *out_ptr(p, row, col0 + col) = (__bf16)sum[i].x;
+        *out_ptr(p, row, col0 + col + 1) = (__bf16)sum[i].y;
+      }
+    }
   }
 }
 
-template <int TB>
+template <int TB, int TPI>
 hipError_t launch_tb(const LinearParams &p, int NW, unsigned grid, hipStream_t stream) {
-  if (NW == 8)
-    hipLaunchKernelGGL((linear_mfma<TB, 8>), dim3(grid), dim3(512), 0, stream, p);
+  if constexpr (TB * TPI > 8) {  // does not fit the register file
+    return hipErrorInvalidValue;
+  } else if (NW == 8)
+    hipLaunchKernelGGL((linear_mfma<TB, 8, TPI>), dim3(grid), dim3(512), 0, stream, p);
   else
-    hipLaunchKernelGGL((linear_mfma<TB, 4>), dim3(grid), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((linear_mfma<TB, 4, TPI>), dim3(grid), dim3(256), 0, stream, p);
   return hipGetLastError();
+}
+
+template <int TPI>
+hipError_t launch_tpi(const LinearParams &p, int NW, unsigned grid, hipStream_t stream) {
+  switch ((p.M + 15) / 16) {
+    case 1: return launch_tb<1, TPI>(p, NW, grid, stream);
+    case 2: return launch_tb<2, TPI>(p, NW, grid, stream);
+    case 3:
+    case 4: return launch_tb<4, TPI>(p, NW, grid, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
 
-hipError_t launch_linear(const LinearParams &p, int NW, unsigned grid, hipStream_t stream) {
-  switch ((p.M + 15) / 16) {
-    case 1: return launch_tb<1>(p, NW, grid, stream);
-    case 2: return launch_tb<2>(p, NW, grid, stream);
-    case 3:
-    case 4: return launch_tb<4>(p, NW, grid, stream);
+hipError_t launch_linear(const LinearParams &p, int NW, int TPI, unsigned grid, hipStream_t stream) {
+  switch (TPI) {
+    case 1: return launch_tpi<1>(p, NW, grid, stream);
+    case 2: return launch_tpi<2>(p, NW, grid, stream);
+    case 4: return launch_tpi<4>(p, NW, grid, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -164,9 +164,12 @@ def test_window_and_append_arguments(lib):
 
 def _linear_ws(M, K, N):
     """Workspace model of gqa_linear: 128-column blocks, k split in whole
-    32-row steps until about 512 workgroups (at least two steps per wave of 4)."""
+    32-row steps into the largest power of two of parts that keeps the grid
+    within 256 workgroups and at least two steps per wave of 4."""
     ntile, ksteps = N // 128, K // 32
-    ks = max(1, min(-(-512 // ntile), ksteps // 8))
+    ks = 1
+    while 2 * ks * ntile <= 256 and 2 * ks <= ksteps // 8:
+        ks *= 2
     per = -(-ksteps // ks)
     ks = -(-ksteps // per)
     return 0 if ks == 1 else 256 * 1024 + ks * M * N * 4
