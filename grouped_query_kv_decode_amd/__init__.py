@@ -12,7 +12,9 @@ Entry points (same names as the C ABI, without the ``gqa_`` prefix):
     decode_window(q, k_cache, v_cache, seq_lens, scale, window, ...)
     decode_append(q, k_new, v_new, k_cache, v_cache, seq_lens, scale, window=0, ...)
     workspace_init(workspace)
-    linear(x, w, out=None, workspace=None)              y = x @ w (bfloat16 projections)
+    linear(x, w, out=None, workspace=None)              y = x @ w (bfloat16 projections, row-major w)
+    pack_weight(w)                                      w in the packed matrix-core layout
+    linear_packed(x, w_packed, N, out=None)             y = x @ w from the packed layout
     decode_layer(x, w_qkv, w_o, k_cache, v_cache, seq_lens, H, G, scale, window=0)
     meanpool_kv(w, H, G, out=None)
     decode_kernel_kind(B, H, G, d, Lmax, dtype)
@@ -24,7 +26,7 @@ import os
 
 __all__ = [
     "GQAError", "decode", "decode_phase", "decode_window", "decode_append", "decode_workspace_size", "workspace_init", "meanpool_kv",
-    "linear", "linear_workspace_size", "decode_layer", "decode_layer_workspace_size", "LayerStep",
+    "linear", "linear_workspace_size", "pack_weight", "linear_packed", "decode_layer", "decode_layer_workspace_size", "LayerStep",
     "decode_kernel_kind", "status_string", "library_path", "load_library", "Decoder",
     "GQA_F32", "GQA_BF16",
 ]
@@ -39,7 +41,8 @@ STATUS_NAMES = {
 }
 EXPORTED = [
     "gqa_decode_workspace_size", "gqa_workspace_init", "gqa_decode", "gqa_decode_phase", "gqa_decode_window",
-    "gqa_decode_append", "gqa_linear_workspace_size", "gqa_linear", "gqa_decode_layer_workspace_size",
+    "gqa_decode_append", "gqa_linear_workspace_size", "gqa_linear", "gqa_pack_weight", "gqa_linear_packed",
+    "gqa_decode_layer_workspace_size",
     "gqa_decode_layer", "gqa_meanpool_kv",
     "gqa_status_string", "gqa_last_hip_error", "gqa_decode_kernel_kind",
 ]
@@ -87,6 +90,10 @@ def load_library(path: str | None = None):
     lib.gqa_linear_workspace_size.argtypes = [ci, ci, ci, ci]
     lib.gqa_linear.restype = ci
     lib.gqa_linear.argtypes = [vp, vp, vp, ci, ci, ci, ci, vp, sz, vp]
+    lib.gqa_pack_weight.restype = ci
+    lib.gqa_pack_weight.argtypes = [vp, vp, ci, ci, ci, vp]
+    lib.gqa_linear_packed.restype = ci
+    lib.gqa_linear_packed.argtypes = [vp, vp, vp, ci, ci, ci, ci, vp]
     lib.gqa_decode_layer_workspace_size.restype = sz
     lib.gqa_decode_layer_workspace_size.argtypes = [ci, ci, ci, ci, ci, ci, ci, ci]
     lib.gqa_decode_layer.restype = ci
@@ -319,6 +326,37 @@ def linear(x, w, out=None, workspace=None):
     return out
 
 
+def pack_weight(w, out=None):
+    """w [K, N] bfloat16 (row-major, on the GPU) in the packed matrix-core
+    layout of gqa_pack_weight (a flat tensor of the same size)."""
+    import torch
+    K, N = w.shape
+    _check_dev("w", w, w, (K, N), torch.bfloat16)
+    if out is None:
+        out = torch.empty(K * N, dtype=torch.bfloat16, device=w.device)
+    _check_dev("out", out, w, (K * N,), torch.bfloat16)
+    st = load_library().gqa_pack_weight(w.data_ptr(), out.data_ptr(), K, N, GQA_BF16, _stream_handle(w.device))
+    if st:
+        raise GQAError(st, "gqa_pack_weight")
+    return out
+
+
+def linear_packed(x, w_packed, N: int, out=None):
+    """y[M,N] = x[M,K] @ W with W given packed (pack_weight)."""
+    import torch
+    M, K = x.shape
+    _check_dev("x", x, x, (M, K), torch.bfloat16)
+    _check_dev("w_packed", w_packed, x, (K * N,), torch.bfloat16)
+    if out is None:
+        out = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    _check_dev("out", out, x, (M, N), torch.bfloat16)
+    st = load_library().gqa_linear_packed(x.data_ptr(), w_packed.data_ptr(), out.data_ptr(), M, K, N, GQA_BF16,
+                                          _stream_handle(x.device))
+    if st:
+        raise GQAError(st, "gqa_linear_packed")
+    return out
+
+
 def decode_layer_workspace_size(B, H, G, d, Lmax, window, d_model, dtype) -> int:
     code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
     return int(load_library().gqa_decode_layer_workspace_size(B, H, G, d, Lmax, window, d_model, code))
@@ -327,7 +365,8 @@ def decode_layer_workspace_size(B, H, G, d, Lmax, window, d_model, dtype) -> int
 class LayerStep:
     """The full decode step (projections, cache append, attention, output
     projection; gqa_decode_layer) bound to fixed tensors and to the stream
-    current at construction."""
+    current at construction.  w_qkv [d_model, (H+2G)d] and w_o [H d, d_model]
+    are row-major; they are packed once here (pack_weight)."""
 
     def __init__(self, x, w_qkv, w_o, k_cache, v_cache, seq_lens, H: int, G: int, scale: float, window: int = 0,
                  out=None, workspace=None):
@@ -352,9 +391,12 @@ class LayerStep:
             raise GQAError(3, "gqa_decode_layer_workspace_size")
         ws_ptr, ws_bytes, self.workspace = _ws_args(need, x.device, workspace)
         self.out = out
-        self._keep = (x, w_qkv, w_o, k_cache, v_cache, seq_lens)
+        self.w_qkv_packed = pack_weight(w_qkv)
+        self.w_o_packed = pack_weight(w_o)
+        self._keep = (x, k_cache, v_cache, seq_lens)
         self._fn = load_library().gqa_decode_layer
-        self._args = (x.data_ptr(), w_qkv.data_ptr(), w_o.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        self._args = (x.data_ptr(), self.w_qkv_packed.data_ptr(), self.w_o_packed.data_ptr(), k_cache.data_ptr(),
+                      v_cache.data_ptr(),
                       seq_lens.data_ptr(), B, H, G, d, Lmax, int(window), d_model, float(scale), GQA_BF16,
                       out.data_ptr(), ws_ptr, ws_bytes, _stream_handle(x.device))
 
@@ -367,8 +409,9 @@ class LayerStep:
 
 def decode_layer(x, w_qkv, w_o, k_cache, v_cache, seq_lens, H: int, G: int, scale: float, window: int = 0,
                  out=None, workspace=None):
-    """y[B, d_model] = one decode step of a GQA attention layer (see LayerStep);
-    the caches receive the new token's keys and values in place."""
+    """y[B, d_model] = one decode step of a GQA attention layer (see LayerStep;
+    the row-major weights are packed on every call - bind a LayerStep to pack
+    them once); the caches receive the new token's keys and values in place."""
     return LayerStep(x, w_qkv, w_o, k_cache, v_cache, seq_lens, H, G, scale, window, out, workspace)()
 
 

@@ -8,6 +8,7 @@
 
 #include "gqa.h"
 #include "gqa_device.h"
+#include "gqa_linear.h"
 
 namespace {
 
@@ -212,26 +213,61 @@ gqa_status linear_impl(const void *x, const void *w, void *const y[3], const int
   return e == hipSuccess ? GQA_OK : hip_fail(e);
 }
 
-// Workspace of the full decode step (gqa_decode_layer): one scratch region
-// (counters + partials) that the three kernels use in turn, then q, the new
-// keys and values, and the attention output.
+// Packed projections: one workgroup per 16-column strip over all of k, so
+// no workspace.  TPI blocks per wave are loaded before they are used.
+gqa_status check_packed(int M, int K, int N, gqa_dtype dt) {
+  if (dt != GQA_F32 && dt != GQA_BF16) return GQA_ERR_UNSUPPORTED;
+  if (M < 0 || K < 1 || N < 1) return GQA_ERR_SHAPE;
+  if (dt != GQA_BF16 || M > 64 || K % 32 != 0 || N % 16 != 0) return GQA_ERR_UNSUPPORTED;
+  if ((unsigned long long)K * N > (1ULL << 40)) return GQA_ERR_SIZE;
+  return GQA_OK;
+}
+
+gqa_status check_layer(int B, int H, int G, int d, int Lmax, int window, int d_model, gqa_dtype dtype) {
+  gqa_status st = check_shape(B, H, G, d, Lmax, dtype);
+  if (st != GQA_OK) return st;
+  if (window < 0 || d_model < 1) return GQA_ERR_SHAPE;
+  st = check_packed(B, d_model, (H + 2 * G) * d, dtype);
+  if (st == GQA_OK) st = check_packed(B, H * d, d_model, dtype);
+  return st;
+}
+
+gqa_status packed_impl(const void *x, const void *wp, void *const y[3], const int seg_lo[4], int nseg, int M, int K,
+                       int N, hipStream_t stream) {
+  gqa::LinearParams p{};
+  p.x = static_cast<const __bf16 *>(x);
+  p.w = static_cast<const __bf16 *>(wp);
+  for (int i = 0; i < 3; ++i) p.y[i] = static_cast<__bf16 *>(y[i]);
+  for (int i = 0; i < 4; ++i) p.seg_lo[i] = seg_lo[i];
+  p.nseg = nseg;
+  p.M = M;
+  p.K = K;
+  p.N = N;
+  const int nw = env_int("GQA_LINEAR_WAVES", 4) == 8 ? 8 : 4;
+  int tpi = env_int("GQA_LINEAR_TPI", 8);
+  if (tpi != 4 && tpi != 8 && tpi != 16) tpi = 8;
+  if (ceil_div(M, 16) > 2 && tpi > 8) tpi = 8;
+  const hipError_t e = gqa::launch_linear_packed(p, nw, tpi, stream);
+  return e == hipSuccess ? GQA_OK : hip_fail(e);
+}
+
+// Workspace of the full decode step (gqa_decode_layer): the decode kernel's
+// scratch (counters + split partials; at least the counter region), then q,
+// the new keys and values, and the attention output.
 struct LayerPlan {
   size_t scratch, q_off, kn_off, vn_off, att_off, total;
 };
 
 gqa_status make_layer_plan(int B, int H, int G, int d, int Lmax, int window, int d_model, LayerPlan *lp) {
+  (void)d_model;
   Plan ap;
   const int Leff = (window > 0 && window < Lmax) ? window : Lmax;
   gqa_status st = make_plan(B, H, G, d, Leff, GQA_BF16, &ap);
   if (st != GQA_OK) return st;
-  LinearPlan l1, l2;
-  st = make_linear_plan(B, d_model, (H + 2 * G) * d, &l1);
-  if (st != GQA_OK) return st;
-  st = make_linear_plan(B, H * d, d_model, &l2);
-  if (st != GQA_OK) return st;
-  size_t scratch = ap.ws_bytes;
-  if (l1.ws_bytes > scratch) scratch = l1.ws_bytes;
-  if (l2.ws_bytes > scratch) scratch = l2.ws_bytes;
+  // The counter region stays reserved even when the attention needs no
+  // split: a workspace may be shared with other calls, which rely on its
+  // first kCounterBytes holding zeroed counters.
+  const size_t scratch = ap.ws_bytes > kCounterBytes ? ap.ws_bytes : kCounterBytes;
   lp->scratch = round_up(scratch, 256);
   lp->q_off = lp->scratch;
   lp->kn_off = lp->q_off + round_up((size_t)B * H * d * 2, 256);
@@ -395,28 +431,46 @@ gqa_status gqa_linear(const void *x, const void *w, void *y, int M, int K, int N
   return linear_impl(x, w, ys, seg, 1, M, K, N, workspace, workspace_bytes, stream);
 }
 
+gqa_status gqa_pack_weight(const void *w, void *w_packed, int K, int N, gqa_dtype dtype, hipStream_t stream) {
+  const gqa_status st = check_packed(1, K, N, dtype);
+  if (st != GQA_OK) return st;
+  if (!w || !w_packed) return GQA_ERR_NULL;
+  if (!aligned(w, 2) || !aligned(w_packed, 16)) return GQA_ERR_ALIGN;
+  if (((unsigned long long)K * N / 8 + 255) / 256 > 0x7fffffffULL) return GQA_ERR_SIZE;
+  const hipError_t e = gqa::launch_pack_weight(w, w_packed, K, N, stream);
+  return e == hipSuccess ? GQA_OK : hip_fail(e);
+}
+
+gqa_status gqa_linear_packed(const void *x, const void *w_packed, void *y, int M, int K, int N, gqa_dtype dtype,
+                             hipStream_t stream) {
+  const gqa_status st = check_packed(M, K, N, dtype);
+  if (st != GQA_OK) return st;
+  if (M == 0) return GQA_OK;
+  if (!x || !w_packed || !y) return GQA_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(w_packed, 16) || !aligned(y, 16)) return GQA_ERR_ALIGN;
+  void *ys[3] = {y, nullptr, nullptr};
+  const int seg[4] = {0, N, N, N};
+  return packed_impl(x, w_packed, ys, seg, 1, M, K, N, stream);
+}
+
 size_t gqa_decode_layer_workspace_size(int B, int H, int G, int d, int Lmax, int window, int d_model,
                                        gqa_dtype dtype) {
-  if (check_shape(B, H, G, d, Lmax, dtype) != GQA_OK || B == 0 || window < 0) return 0;
-  if (check_linear(B, d_model, (H + 2 * G) * d, dtype) != GQA_OK || check_linear(B, H * d, d_model, dtype) != GQA_OK)
-    return 0;
+  if (check_layer(B, H, G, d, Lmax, window, d_model, dtype) != GQA_OK || B == 0) return 0;
   LayerPlan lp;
   return make_layer_plan(B, H, G, d, Lmax, window, d_model, &lp) == GQA_OK ? lp.total : 0;
 }
 
-gqa_status gqa_decode_layer(const void *x, const void *w_qkv, const void *w_o, void *k_cache, void *v_cache,
-                            const int32_t *seq_lens, int B, int H, int G, int d, int Lmax, int window, int d_model,
-                            float scale, gqa_dtype dtype, void *y, void *workspace, size_t workspace_bytes,
-                            hipStream_t stream) {
-  gqa_status st = check_shape(B, H, G, d, Lmax, dtype);
-  if (st != GQA_OK) return st;
-  if (window < 0 || d_model < 1) return GQA_ERR_SHAPE;
-  st = check_linear(B, d_model, (H + 2 * G) * d, dtype);
-  if (st == GQA_OK) st = check_linear(B, H * d, d_model, dtype);
+gqa_status gqa_decode_layer(const void *x, const void *w_qkv_packed, const void *w_o_packed, void *k_cache,
+                            void *v_cache, const int32_t *seq_lens, int B, int H, int G, int d, int Lmax, int window,
+                            int d_model, float scale, gqa_dtype dtype, void *y, void *workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  gqa_status st = check_layer(B, H, G, d, Lmax, window, d_model, dtype);
   if (st != GQA_OK) return st;
   if (B == 0) return GQA_OK;
-  if (!x || !w_qkv || !w_o || !k_cache || !v_cache || !seq_lens || !y || !workspace) return GQA_ERR_NULL;
-  if (!aligned(x, 16) || !aligned(w_qkv, 16) || !aligned(w_o, 16) || !aligned(y, 16)) return GQA_ERR_ALIGN;
+  if (!x || !w_qkv_packed || !w_o_packed || !k_cache || !v_cache || !seq_lens || !y || !workspace)
+    return GQA_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(w_qkv_packed, 16) || !aligned(w_o_packed, 16) || !aligned(y, 16))
+    return GQA_ERR_ALIGN;
   if (!aligned(workspace, 256)) return GQA_ERR_ALIGN;
   LayerPlan lp;
   st = make_layer_plan(B, H, G, d, Lmax, window, d_model, &lp);
@@ -427,7 +481,7 @@ gqa_status gqa_decode_layer(const void *x, const void *w_qkv, const void *w_o, v
   // 1. q, key, val = x @ [Wq | Wk | Wv], written as three tensors
   void *ys[3] = {q, kn, vn};
   const int seg[4] = {0, H * d, (H + G) * d, (H + 2 * G) * d};
-  st = linear_impl(x, w_qkv, ys, seg, 3, B, d_model, (H + 2 * G) * d, ws, lp.scratch, stream);
+  st = packed_impl(x, w_qkv_packed, ys, seg, 3, B, d_model, (H + 2 * G) * d, stream);
   if (st != GQA_OK) return st;
   // 2. append the new key/value to the caches, attend
   st = decode_impl(0, q, kn, vn, k_cache, v_cache, seq_lens, B, H, G, d, Lmax, window, scale, dtype, att, ws,
@@ -436,7 +490,7 @@ gqa_status gqa_decode_layer(const void *x, const void *w_qkv, const void *w_o, v
   // 3. y = out @ Wo
   void *yo[3] = {y, nullptr, nullptr};
   const int seg_o[4] = {0, d_model, d_model, d_model};
-  return linear_impl(att, w_o, yo, seg_o, 1, B, H * d, d_model, ws, lp.scratch, stream);
+  return packed_impl(att, w_o_packed, yo, seg_o, 1, B, H * d, d_model, stream);
 }
 
 gqa_status gqa_meanpool_kv(const float *w, int d_model, int H, int G, int h, float *w_out, hipStream_t stream) {

@@ -36,19 +36,6 @@ struct DecodeParams {
   float scale_log2;        // scale * log2(e): scores are kept in log2 units
 };
 
-// Projection y[M, N] = x[M, K] @ W[K, N] (bfloat16, row-major).
-struct LinearParams {
-  const __bf16 *x;   // [M, K]
-  const __bf16 *w;   // [K, N]
-  __bf16 *y[3];      // output segments (see seg_lo)
-  int seg_lo[4];     // output column c in [seg_lo[s], seg_lo[s+1]) goes to y[s], row stride seg_lo[s+1]-seg_lo[s]
-  int nseg;
-  float *ws_part;    // [KS, M, N] k-split partial sums
-  unsigned *ws_cnt;  // arrival counter per 128-column block; zero between calls
-  int M, K, N;
-  int KS;            // k splits
-  int ksteps_per_split;  // 32-row steps per split
-};
 
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kNegInf = -__builtin_inff();
@@ -200,7 +187,6 @@ __device__ void merge_heads(const DecodeParams &p, int b, int head0, int nh, int
 hipError_t launch_decode_valu(const DecodeParams &p, int dtype, int D, int RC, unsigned grid, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeParams &p, int D, int HB, int NW, unsigned grid, hipStream_t stream);
 hipError_t launch_merge(const DecodeParams &p, int dtype, int D, int heads_per_unit, hipStream_t stream);
-hipError_t launch_linear(const LinearParams &p, int NW, int TPI, unsigned grid, hipStream_t stream);
 hipError_t launch_meanpool(const float *w, int d_model, int H, int G, int h, float *w_out, hipStream_t stream);
 hipError_t launch_fill_zero(void *ptr, size_t bytes, hipStream_t stream);
 

@@ -17,6 +17,7 @@
 // column block last (same arrival protocol as the decode kernel), so the
 // result is deterministic.
 #include "gqa_device.h"
+#include "gqa_linear.h"
 
 namespace gqa {
 namespace {

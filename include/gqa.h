@@ -184,33 +184,62 @@ gqa_status gqa_linear(const void *x, const void *w, void *y, int M, int K, int N
                       size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Weight layout for the matrix cores (a one-time conversion of a model's
+ * projection weights, like gqa_meanpool_kv): w [K, N] bfloat16 row-major is
+ * rewritten into w_packed (same size, K*N*2 bytes) as 32 x 16 blocks:
+ *   block (kb, nb), kb < K/32, nb < N/16, starts at element (kb*(N/16) + nb)*512;
+ *   inside it, element 8*l + e (l = 16c + n, c < 4, n < 16, e < 8) is
+ *   w[32kb + 8c + e][16nb + n].
+ * A wave then fetches the A operand of one v_mfma_f32_16x16x32_bf16 as one
+ * contiguous 1 KiB load, and the workgroups of the product (one per 16-column
+ * strip) together read contiguous bands of rows.
+ *   K a multiple of 32, N a multiple of 16, dtype GQA_BF16
+ *   (GQA_ERR_UNSUPPORTED otherwise; GQA_ERR_SHAPE for K or N < 1).
+ *   w 2-byte aligned, w_packed 16-byte aligned, not overlapping.
+ * Status codes as for gqa_decode.
+ */
+gqa_status gqa_pack_weight(const void *w, void *w_packed, int K, int N, gqa_dtype dtype, hipStream_t stream);
+
+/*
+ * gqa_linear over a packed weight (gqa_pack_weight): y[M, N] = x[M, K] @ W.
+ * One workgroup per 16-column strip reads the strip once over all of K, so
+ * no workspace is needed and each output is one binary32 sum (in a fixed
+ * order) rounded once to bfloat16.
+ *   x [M, K], y [M, N] bfloat16 row-major, 16-byte aligned; M in 0..64
+ *   (0 is a no-op); K a multiple of 32; N a multiple of 16; dtype GQA_BF16.
+ * Status codes as for gqa_linear.
+ */
+gqa_status gqa_linear_packed(const void *x, const void *w_packed, void *y, int M, int K, int N, gqa_dtype dtype,
+                             hipStream_t stream);
+
+/*
  * The whole decode-step block of wikillm "Grouped-query attention (GQA)"
  * (Implementation sketch) for B sequences, one new token each, enqueued as
  * three kernels on `stream`:
- *   1. [q | key | val] = x @ w_qkv           (gqa_linear, output split in three)
+ *   1. [q | key | val] = x @ w_qkv           (gqa_linear_packed, output split in three)
  *   2. key/val appended at row len_b - 1 of the caches; out = attention
  *      (gqa_decode_append, with `window` as there)
- *   3. y = out @ w_o                           (gqa_linear)
- *   x      [B, d_model] bfloat16, device: the token's hidden state.
- *   w_qkv  [d_model, (H + 2G) d] bfloat16: columns H d of query heads, then G d
- *          of key heads, then G d of value heads (head i owns d columns).
- *   w_o    [H d, d_model] bfloat16.
+ *   3. y = out @ w_o                           (gqa_linear_packed)
+ *   x             [B, d_model] bfloat16, device: the token's hidden state.
+ *   w_qkv_packed  [d_model, (H + 2G) d] bfloat16 in the packed layout
+ *                 (gqa_pack_weight): columns H d of query heads, then G d of
+ *                 key heads, then G d of value heads (head i owns d columns).
+ *   w_o_packed    [H d, d_model] bfloat16, packed.
  *   k_cache, v_cache, seq_lens, B, H, G, d, Lmax, window, scale: as for
- *          gqa_decode_append (caches updated in place).
- *   y      [B, d_model] bfloat16.
+ *                 gqa_decode_append (caches updated in place).
+ *   y             [B, d_model] bfloat16.
  * q, key, val and out are rounded to bfloat16 between the steps (they live in
- * the workspace).  dtype must be GQA_BF16, B <= 64, d_model and (H + 2G) d
- * multiples of 128, H d a multiple of 32 (GQA_ERR_UNSUPPORTED otherwise).
- * Other status codes as for gqa_decode.  Workspace:
- * gqa_decode_layer_workspace_size(...) bytes, 256-byte aligned, cleared once
- * with gqa_workspace_init.
+ * the workspace).  dtype must be GQA_BF16, B <= 64 and d_model a multiple of
+ * 32 (GQA_ERR_UNSUPPORTED otherwise).  Other status codes as for gqa_decode.
+ * Workspace: gqa_decode_layer_workspace_size(...) bytes, 256-byte aligned,
+ * cleared once with gqa_workspace_init.
  */
 size_t gqa_decode_layer_workspace_size(int B, int H, int G, int d, int Lmax, int window, int d_model,
                                        gqa_dtype dtype);
-gqa_status gqa_decode_layer(const void *x, const void *w_qkv, const void *w_o, void *k_cache, void *v_cache,
-                            const int32_t *seq_lens, int B, int H, int G, int d, int Lmax, int window, int d_model,
-                            float scale, gqa_dtype dtype, void *y, void *workspace, size_t workspace_bytes,
-                            hipStream_t stream);
+gqa_status gqa_decode_layer(const void *x, const void *w_qkv_packed, const void *w_o_packed, void *k_cache,
+                            void *v_cache, const int32_t *seq_lens, int B, int H, int G, int d, int Lmax, int window,
+                            int d_model, float scale, gqa_dtype dtype, void *y, void *workspace,
+                            size_t workspace_bytes, hipStream_t stream);
 
 /*
  * The pages' checkpoint conversion step, numeric core only: wikillm

@@ -10,3 +10,23 @@ for p in (_ROOT, _TESTS):
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+
+
+import pytest  # noqa: E402
+
+
+@pytest.fixture(autouse=True)
+def _counters_zero_between_calls(request):
+    """After every GPU test: each workspace the binding cached still holds
+    zeroed arrival counters in its first 256 KiB, the state every call must
+    leave behind for the next call on that workspace."""
+    yield
+    if request.node.get_closest_marker("gpu") is None:
+        return
+    import torch
+    import grouped_query_kv_decode_amd as gqa
+    torch.cuda.synchronize()
+    for key, ws in gqa._ws_cache.items():
+        head = ws[:min(ws.numel(), 256 * 1024) // 4 * 4].cpu().view(torch.int32)
+        nz = head.nonzero().flatten()[:8].tolist()
+        assert not nz, "workspace %s: counters left non-zero at int32 index %s" % (key, nz)

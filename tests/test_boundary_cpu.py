@@ -202,16 +202,44 @@ def test_linear_workspace_model(lib):
     assert lib.gqa_linear_workspace_size(0, 4096, 4096, BF16) == 0
 
 
+def test_pack_and_linear_packed_arguments(lib):
+    pack = lambda w=P, wp=P, K=64, N=32, dt=BF16: lib.gqa_pack_weight(w, wp, K, N, dt, None)
+    assert pack(dt=F32) == UNSUP
+    assert pack(K=48) == UNSUP
+    assert pack(N=24) == UNSUP
+    assert pack(K=0) == SHAPE
+    assert pack(N=-16) == SHAPE
+    assert pack(w=None) == NULL
+    assert pack(wp=None) == NULL
+    assert pack(w=P + 1) == ALIGN
+    assert pack(wp=P + 8) == ALIGN
+    lin = lambda x=P, wp=P, y=P, M=4, K=64, N=32, dt=BF16: lib.gqa_linear_packed(x, wp, y, M, K, N, dt, None)
+    assert lin(dt=F32) == UNSUP
+    assert lin(M=65) == UNSUP
+    assert lin(K=40) == UNSUP
+    assert lin(N=8) == UNSUP
+    assert lin(M=-1) == SHAPE
+    assert lin(M=0, x=None, wp=None, y=None) == OK
+    assert lin(wp=None) == NULL
+    assert lin(x=P + 2) == ALIGN
+    assert lin(y=P + 8) == ALIGN
+
+
 def test_decode_layer_arguments(lib):
     # Mistral-7B shape: d_model 4096, H 32, G 8, d 128
     need = lib.gqa_decode_layer_workspace_size(16, 32, 8, 128, 4096, 0, 4096, BF16)
     att = lib.gqa_decode_workspace_size(16, 32, 8, 128, 4096, BF16)
-    scratch = max(att, _linear_ws(16, 4096, 6144), _linear_ws(16, 32 * 128, 4096))
+    scratch = max(att, 256 * 1024)  # the packed projections need no workspace; counters always reserved
     bufs = 2 * (16 * 32 * 128) * 2 + 2 * (16 * 8 * 128) * 2
     assert need == -(-scratch // 256) * 256 + bufs
+    # a window short enough for one split: no attention scratch, but the
+    # buffers still start after the 256 KiB counter region
+    assert lib.gqa_decode_workspace_size(3, 8, 2, 128, 100, BF16) == 0
+    assert lib.gqa_decode_layer_workspace_size(3, 8, 2, 128, 600, 100, 512, BF16) == \
+        256 * 1024 + 2 * 256 * (-(-3 * 8 * 128 * 2 // 256)) + 2 * 256 * (-(-3 * 2 * 128 * 2 // 256))
     assert lib.gqa_decode_layer_workspace_size(16, 32, 8, 128, 4096, 0, 4096, F32) == 0
     assert lib.gqa_decode_layer_workspace_size(65, 32, 8, 128, 4096, 0, 4096, BF16) == 0
-    assert lib.gqa_decode_layer_workspace_size(16, 32, 8, 128, 4096, 0, 4000, BF16) == 0
+    assert lib.gqa_decode_layer_workspace_size(16, 32, 8, 128, 4096, 0, 4008, BF16) == 0
 
     def layer(x=P, w1=P, w2=P, B=2, H=8, G=2, d=128, W=0, dm=1024, dt=BF16, ws=P, nb=1 << 30):
         return lib.gqa_decode_layer(x, w1, w2, P, P, P, B, H, G, d, 512, W, dm, 0.125, dt, P, ws, nb, None)

@@ -6,6 +6,10 @@ gqa_linear: every output is one binary32 sum rounded once to bfloat16, so
 (half an ulp of bfloat16 for the rounding, plus a generous bound on binary32
 accumulation error; a wrong operand or index is off by O(|oracle|)).
 
+gqa_linear_packed (weights in the packed layout of gqa_pack_weight): the
+same bound.  gqa_pack_weight: bit-exact against the layout built by host
+reshapes.
+
 gqa_decode_layer: element-wise parity holds stage by stage - the one-call
 step is bit-equal to the three public entry points called in turn, and each
 of those is checked against the oracle on identical inputs (here and in
@@ -139,6 +143,80 @@ def test_linear_special_values(ksplit):
     assert torch.equal(y[3], x[3, :N])
 
 
+# --------------------------------------------------------------- packed weights
+
+def host_pack(w):
+    """The packed layout of gqa_pack_weight, by host reshapes: element
+    (kb, nb, c, n, e) = w[32kb + 8c + e, 16nb + n]."""
+    K, N = w.shape
+    return w.reshape(K // 32, 4, 8, N // 16, 16).permute(0, 3, 1, 4, 2).reshape(-1).contiguous()
+
+
+@pytest.mark.parametrize("shape", [(32, 16), (64, 48), (4096, 6144), (96, 4096)])
+def test_pack_weight_layout(shape):
+    K, N = shape
+    w = rand_bf16((K, N), seed=K + N)
+    wp = gqa.pack_weight(w.to(DEV)).cpu()
+    torch.cuda.synchronize()
+    assert torch.equal(wp.view(torch.int16), host_pack(w).view(torch.int16))
+
+
+PACKED_CASES = [
+    # (M, K, N)
+    (1, 32, 16),             # one block
+    (5, 96, 48),             # ragged tokens, three strips
+    (16, 4096, 6144),        # fused q/k/v projection, d_model 4096, H 32, G 8, d 128
+    (16, 4096, 4096),        # output projection of the same layer
+    (17, 1024, 272),         # two token tiles
+    (33, 512, 640),          # three token tiles (rounded up to four)
+    (64, 4096, 128),         # most tokens
+    (3, 8192, 1024),
+    (2, 4096, 1088),         # fused projection of H 16, G 1, d 64
+]
+
+
+@pytest.mark.parametrize("case", PACKED_CASES, ids=lambda c: "M%d_K%d_N%d" % c)
+@pytest.mark.parametrize("plan", [(None, None), ("4", "4"), ("8", "16"), ("8", "8")], ids=["default", "w4t4",
+                                                                                          "w8t16", "w8t8"])
+def test_linear_packed_parity(monkeypatch, case, plan):
+    M, K, N = case
+    for name, v in (("GQA_LINEAR_WAVES", plan[0]), ("GQA_LINEAR_TPI", plan[1])):
+        if v is None:
+            monkeypatch.delenv(name, raising=False)
+        else:
+            monkeypatch.setenv(name, v)
+    x = rand_bf16((M, K), seed=M + K)
+    w = rand_bf16((K, N), seed=N + 7, std=K ** -0.5)
+    wp = gqa.pack_weight(w.to(DEV))
+    y = gqa.linear_packed(x.to(DEV), wp, N)
+    torch.cuda.synchronize()
+    check_linear(y, x, w, "linear_packed M%d K%d N%d plan=%s" % (M, K, N, plan))
+
+
+def test_linear_packed_special_values():
+    M, K, N = 4, 256, 256
+    x = rand_bf16((M, K), seed=31)
+    x[1] = 0
+    x[2, 17] = float("nan")
+    w = torch.eye(N, dtype=torch.bfloat16)
+    y = gqa.linear_packed(x.to(DEV), gqa.pack_weight(w.to(DEV)), N).cpu()
+    torch.cuda.synchronize()
+    assert torch.equal(y[0], x[0])
+    assert torch.equal(y[1], torch.zeros(N, dtype=torch.bfloat16))
+    assert torch.isnan(y[2]).all()
+    assert torch.equal(y[3], x[3])
+
+
+def test_linear_packed_deterministic():
+    M, K, N = 16, 4096, 6144
+    x = rand_bf16((M, K), seed=41).to(DEV)
+    wp = gqa.pack_weight(rand_bf16((K, N), seed=42, std=K ** -0.5).to(DEV))
+    a = gqa.linear_packed(x, wp, N).clone()
+    b = gqa.linear_packed(x, wp, N)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
 # --------------------------------------------------------------- full decode step
 
 LAYER_CASES = [
@@ -165,12 +243,12 @@ def composed(x, w_qkv, w_o, k, v, lens, H, G, scale, window):
     """The same step from the public entry points, one call at a time."""
     B = x.shape[0]
     d = k.shape[3]
-    qkv = gqa.linear(x, w_qkv)
+    qkv = gqa.linear_packed(x, gqa.pack_weight(w_qkv), w_qkv.shape[1])
     q = qkv[:, :H * d].reshape(B, H, d).contiguous()
     kn = qkv[:, H * d:(H + G) * d].reshape(B, G, d).contiguous()
     vn = qkv[:, (H + G) * d:].reshape(B, G, d).contiguous()
     att = gqa.decode_append(q, kn, vn, k, v, lens, scale, window=window)
-    return gqa.linear(att.reshape(B, H * d), w_o)
+    return gqa.linear_packed(att.reshape(B, H * d), gqa.pack_weight(w_o), w_o.shape[1])
 
 
 def check_layer(y, ref, what):
