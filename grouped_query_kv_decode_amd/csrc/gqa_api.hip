@@ -89,10 +89,19 @@ gqa_status make_plan(int B, int H, int G, int d, int Lmax, gqa_dtype dt, Plan *p
   pl->NW = 4;
   if (kind == KIND_MFMA) {
     const int hb = (r + 15) / 16;
-    pl->HB = hb <= 1 ? 1 : (hb <= 2 ? 2 : 4);
+    const int hb_all = hb <= 1 ? 1 : (hb <= 2 ? 2 : 4);
+    // Spread the head blocks over workgroups when there are fewer (b, g)
+    // units than compute units: a workgroup's tile loop serves each of its
+    // head blocks in turn, so with few units the loop, not HBM, sets the pace.
+    int hc = ((long)B * G < 256) ? hb_all : 1;
+    const int hc_env = env_int("GQA_HEAD_SPLIT", 0);
+    if (hc_env == 1 || hc_env == 2 || hc_env == 4) hc = hc_env;
+    if (hc > hb_all) hc = hb_all;
+    while (hc > 1 && (hc - 1) * (hb_all / hc) * 16 >= r) hc /= 2;  // no chunk without heads
+    pl->HC = hc;
+    pl->HB = hb_all / hc;
     pl->NW = 4;  // chosen below, once the split length is known
     pl->RC = 0;
-    pl->HC = 1;
   } else {
     pl->RC = next_pow2(r < 8 ? r : 8);
     pl->HC = ceil_div(r, pl->RC);

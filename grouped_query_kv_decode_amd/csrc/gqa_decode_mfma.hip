@@ -88,14 +88,22 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma(DecodeParams p) {
 
   // Split index slowest: consecutive workgroups (which the dispatcher deals
   // round-robin to the XCDs) are different (b, g) units of one split, so
-  // every XCD gets an even share of the units whatever their lengths.
-  const unsigned units = (unsigned)p.B * p.G;
+  // every XCD gets an even share of the units whatever their lengths.  With
+  // the group's head blocks spread over p.HC workgroups (head chunk hc), the
+  // chunks of one (b, g, split) are B*G apart in dispatch order - on the same
+  // XCD when B*G is a multiple of 8, so the tiles they all read come from
+  // that XCD's L2 after the first.
+  const unsigned bg = (unsigned)p.B * p.G;
+  const unsigned units = bg * p.HC;
   const int s = blockIdx.x / units;
-  const unsigned u = blockIdx.x % units;
+  const unsigned rem = blockIdx.x % units;
+  const int hc = rem / bg;
+  const unsigned u = rem % bg;
   const int g = u % p.G;
   const int b = u / p.G;
 
-  const int head0 = g * p.r;
+  const int head0 = g * p.r + hc * 16 * HB;
+  const int rw = min(p.r - hc * 16 * HB, 16 * HB);  // query heads of this workgroup
   const int t0 = s * p.chunk;
 
   // B operand of the score MFMAs: q of head hb*16 + nn, dims kb*32 + 8c .. +7.
@@ -106,7 +114,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma(DecodeParams p) {
     const __bf16 *qp = static_cast<const __bf16 *>(p.q) + ((size_t)b * p.H + head0 + j) * D + 8 * c;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
-      qB[hb][kb] = j < p.r ? *reinterpret_cast<const u32x4 *>(qp + kb * 32) : u32x4{0u, 0u, 0u, 0u};
+      qB[hb][kb] = j < rw ? *reinterpret_cast<const u32x4 *>(qp + kb * 32) : u32x4{0u, 0u, 0u, 0u};
   }
 
   const size_t slab = ((size_t)b * p.G + g) * (size_t)p.Lmax * D;
@@ -154,7 +162,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma(DecodeParams p) {
   const int nsplit = num_splits(n - lo, p.chunk);
   if (s >= nsplit) return;
   if (n == 0) {
-    write_zero_heads<__bf16, D>(p, b, head0, p.r);
+    write_zero_heads<__bf16, D>(p, b, head0, rw);
     return;
   }
   const int ts = lo + t0;  // this split: positions [ts, t1)
@@ -163,7 +171,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma(DecodeParams p) {
   // must end before it, the tile holding it takes the per-row path.
   const bool append = p.k_new != nullptr;
   const int t_full = append ? min(t1, n - 1) : t1;
-  if (append && s == nsplit - 1) append_row<__bf16, D>(p, b, g, n);
+  if (append && s == nsplit - 1 && hc == 0) append_row<__bf16, D>(p, b, g, n);
   const __bf16 *knew = append ? static_cast<const __bf16 *>(p.k_new) + ((size_t)b * p.G + g) * D : nullptr;
   const __bf16 *vnew = append ? static_cast<const __bf16 *>(p.v_new) + ((size_t)b * p.G + g) * D : nullptr;
 
@@ -344,7 +352,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma(DecodeParams p) {
     }
   }
 
-  for (int idx = threadIdx.x; idx < p.r * (D / 4); idx += blockDim.x) {
+  for (int idx = threadIdx.x; idx < rw * (D / 4); idx += blockDim.x) {
     const int j = idx / (D / 4), cc = (idx % (D / 4)) * 4;
     float M = sm_m[0][j];
 #pragma unroll
@@ -381,8 +389,8 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma(DecodeParams p) {
     }
   }
   if (nsplit == 1 || !p.fused) return;
-  if (!arrive_last(p.ws_cnt + (size_t)b * p.G + g, nsplit)) return;
-  merge_heads<__bf16, D>(p, b, head0, p.r, nsplit);
+  if (!arrive_last(p.ws_cnt + ((size_t)b * p.G + g) * p.HC + hc, nsplit)) return;
+  merge_heads<__bf16, D>(p, b, head0, rw, nsplit);
 }
 
 template <int D, int HB, int NW>

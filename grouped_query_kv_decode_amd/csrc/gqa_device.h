@@ -32,7 +32,8 @@ struct DecodeParams {
   int r;                   // query heads per K/V head, H / G
   int S;                   // splits per (b, g) in the grid
   int chunk;               // positions per split
-  int HC;                  // head chunks per (b, g) in the grid (VALU kernel)
+  int HC;                  // head chunks per (b, g) in the grid (VALU kernel: RC heads each;
+                           // matrix-core kernel: its HB head blocks of 16 each)
   float scale_log2;        // scale * log2(e): scores are kept in log2 units
 };
 

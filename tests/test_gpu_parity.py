@@ -40,7 +40,7 @@ def env(monkeypatch):
             else:
                 monkeypatch.setenv(k, str(v))
     set_(GQA_KERNEL=None, GQA_CHUNK=None, GQA_TARGET_WGS=None, GQA_MAX_CHUNK=None, GQA_MERGE=None, GQA_WAVES=None,
-         GQA_CONTIG=None)
+         GQA_CONTIG=None, GQA_HEAD_SPLIT=None)
     return set_
 
 
@@ -154,6 +154,46 @@ def test_launch_variants(env, waves, contig, case):
         env(GQA_WAVES=waves, GQA_CONTIG=contig, GQA_CHUNK=chunk)
         out = run_gpu(q, k, v, lens_t, scale)
         check(out, ref, "bf16", "waves=%d contig=%d chunk=%s %s" % (waves, contig, chunk, case[:5]))
+
+
+HEAD_SPLIT_CASES = [
+    # (B, H, G, d, Lmax, lens): r = 64, 24, 48 and 40 (last head chunk partly empty)
+    (3, 64, 1, 64, 1500, [1500, 513, 7]),
+    (2, 24, 1, 128, 900, [900, 300]),
+    (2, 48, 1, 64, 700, [700, 1]),
+    (2, 80, 2, 128, 600, [600, 333]),
+]
+
+
+@pytest.mark.parametrize("case", HEAD_SPLIT_CASES, ids=lambda c: "H%d_G%d_d%d" % c[1:4])
+@pytest.mark.parametrize("split", [1, 2, 4])
+@pytest.mark.parametrize("merge", ["fused", "kernel"])
+def test_head_split(env, case, split, merge):
+    """The matrix-core kernel with the group's head blocks spread over 1, 2
+    or 4 workgroups (the planner drops to a split that leaves no workgroup
+    without heads), fused or separate merge, against the oracle."""
+    env(GQA_HEAD_SPLIT=split, GQA_CHUNK=256, GQA_MERGE=None if merge == "fused" else "kernel")
+    q, k, v, lens, scale = rand_case(*case, "bf16", seed=sum(case[:5]) + split)
+    out = run_gpu(q, k, v, lens, scale)
+    check(out, oracle_out(q, k, v, lens, scale), "bf16", "head split %d %s %s" % (split, merge, case[:5]))
+
+
+@pytest.mark.parametrize("split", [1, 4])
+def test_head_split_append_and_window(env, split):
+    env(GQA_HEAD_SPLIT=split, GQA_CHUNK=256)
+    B, H, G, d, L = 3, 64, 1, 64, 1100
+    lens = [1100, 700, 1]
+    q, k, v, lt, scale = rand_case(B, H, G, d, L, lens, "bf16", seed=900 + split)
+    gen = torch.Generator(DEV).manual_seed(split)
+    kn = torch.randn((B, G, d), generator=gen, device=DEV).to(torch.bfloat16)
+    vn = torch.randn((B, G, d), generator=gen, device=DEV).to(torch.bfloat16)
+    k0, v0 = k.cpu(), v.cpu()
+    out = gqa.decode_append(q, kn, vn, k, v, lt, scale, window=300)
+    torch.cuda.synchronize()
+    ref, rk, rv = oracle.decode_append(q.cpu(), kn.cpu(), vn.cpu(), k0, v0, lt.cpu(), scale, window=300)
+    check(out, ref, "bf16", "head split %d append+window" % split)
+    assert np.array_equal(k.cpu().view(torch.int16).numpy().view(np.uint16), rk.view(np.uint16))
+    assert np.array_equal(v.cpu().view(torch.int16).numpy().view(np.uint16), rv.view(np.uint16))
 
 
 @pytest.mark.parametrize("kernel", ["default", "valu"])
