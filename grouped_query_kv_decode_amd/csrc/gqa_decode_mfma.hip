@@ -132,6 +132,9 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma(DecodeParams p) {
     VRow vR[8];
   };
   // A whole tile inside the split: tile base is uniform, lane offsets fixed.
+  // The cache is read once per call, so its loads are non-temporal: the
+  // stream then does not evict what is reused (q, partial sums, counters)
+  // from the caches, which measured 10% faster on a 268 MB cache.
   auto load_full = [&](Tile &T, int tt) {
     const __bf16 *kt = kbase + (size_t)tt * D;
     const __bf16 *vt = vbase + (size_t)tt * D;
@@ -139,9 +142,9 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma(DecodeParams p) {
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
-        T.kA[h][kb] = *reinterpret_cast<const u32x4 *>(kt + koff + h * 4 * D + kb * 32);
+        T.kA[h][kb] = stream_load(reinterpret_cast<const u32x4 *>(kt + koff + h * 4 * D + kb * 32));
 #pragma unroll
-    for (int u = 0; u < 8; ++u) T.vR[u] = *reinterpret_cast<const VRow *>(vt + voff + u * D);
+    for (int u = 0; u < 8; ++u) T.vR[u] = stream_load(reinterpret_cast<const VRow *>(vt + voff + u * D));
   };
 
   // The wave's first tile is requested before the sequence length arrives
@@ -194,13 +197,13 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma(DecodeParams p) {
       const int t = min(tt + 8 * (nn >> 2) + 4 * h + (nn & 3), t1 - 1);
       const __bf16 *src = (append && t == n - 1) ? knew : kbase + (size_t)t * D;
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) T.kA[h][kb] = *reinterpret_cast<const u32x4 *>(src + 8 * c + kb * 32);
+      for (int kb = 0; kb < KB; ++kb) T.kA[h][kb] = stream_load(reinterpret_cast<const u32x4 *>(src + 8 * c + kb * 32));
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int t = min(tt + 8 * c + u, t1 - 1);
       const __bf16 *src = (append && t == n - 1) ? vnew : vbase + (size_t)t * D;
-      T.vR[u] = *reinterpret_cast<const VRow *>(src + VPL * nn);
+      T.vR[u] = stream_load(reinterpret_cast<const VRow *>(src + VPL * nn));
     }
   };
   // Scores, softmax weights and the weighted V sum of one tile.  The running

@@ -128,8 +128,8 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeParams p) {
       ok[u] = t < t1;
       const int row = ok[u] ? t : t1 - 1;  // never past the length
       const bool fresh = append && row == n - 1;
-      kr[u] = *reinterpret_cast<const uint4 *>(fresh ? knew : kp + (size_t)row * D);
-      vr[u] = *reinterpret_cast<const uint4 *>(fresh ? vnew : vp + (size_t)row * D);
+      kr[u] = stream_load(reinterpret_cast<const uint4 *>(fresh ? knew : kp + (size_t)row * D));
+      vr[u] = stream_load(reinterpret_cast<const uint4 *>(fresh ? vnew : vp + (size_t)row * D));
     }
     float sc[U][RC];
 #pragma unroll

@@ -43,6 +43,16 @@ constexpr float kNegInf = -__builtin_inff();
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// A load of data that is read once (KV cache, weights): non-temporal, so it
+// streams through the caches without displacing data that is reused.
+template <typename V>
+__device__ __forceinline__ V stream_load(const V *p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ uint4 stream_load(const uint4 *p) {
+  typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 // Shift used with a running maximum: keeps exp2(x - shift) free of
 // (-inf) - (-inf) when nothing has been seen yet.
 __device__ __forceinline__ float safe_shift(float m) { return m == kNegInf ? 0.f : m; }

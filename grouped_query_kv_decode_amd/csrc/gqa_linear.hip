@@ -82,7 +82,7 @@ __global__ __launch_bounds__(64 * NW) void linear_mfma(LinearParams p) {
       const int k = min(base + j * NW, kstep1 - 1) * 32;
       const __bf16 *wk = wl + (size_t)k * p.N;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) wR[j][u] = *reinterpret_cast<const u32x4 *>(wk + (size_t)u * p.N);
+      for (int u = 0; u < 8; ++u) wR[j][u] = stream_load(reinterpret_cast<const u32x4 *>(wk + (size_t)u * p.N));
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb) {
         const int row = tb * 16 + nn;

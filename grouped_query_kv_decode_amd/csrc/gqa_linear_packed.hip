@@ -74,7 +74,7 @@ __global__ __launch_bounds__(64 * NW) void linear_packed(LinearParams p) {
 #pragma unroll
     for (int j = 0; j < TPI; ++j) {
       const int kb = min(base + j * NW, kblocks - 1);  // past the end: re-read the last block, skipped below
-      a[j] = *reinterpret_cast<const u32x4 *>(wl + (size_t)kb * nstrips * 512);
+      a[j] = stream_load(reinterpret_cast<const u32x4 *>(wl + (size_t)kb * nstrips * 512));
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb) {
         const int row = tb * 16 + nn;
