@@ -67,9 +67,10 @@ gqa_status check_shape(int B, int H, int G, int d, int Lmax, gqa_dtype dt) {
 //  - kernel: bfloat16 uses the matrix-core kernel for r = H/G in 2..64 and
 //    the VALU kernel for r = 1, where it measured faster (no 16-head padding);
 //    fp32 always uses the VALU kernel.  GQA_KERNEL=valu|mfma overrides.
-//  - workgroups of the matrix-core kernel have 8 waves for d = 64 or splits
-//    longer than 2048 positions, else 4 (GQA_WAVES = 4, 8 or 16 overrides),
-//    capped by the register budget for the group's head blocks.
+//  - workgroups of the matrix-core kernel have 4 waves (GQA_WAVES = 8 or 16
+//    overrides where the register budget for the head blocks allows).
+//  - with fewer (b, g) units than compute units the matrix-core kernel
+//    spreads a group's head blocks over 2 or 4 workgroups (GQA_HEAD_SPLIT).
 //  - splits: one workgroup per (b, g, head chunk, split).  The split length
 //    is chosen so that the grid holds about GQA_TARGET_WGS = 256 workgroups
 //    (one per compute unit), clamped to [512, GQA_MAX_CHUNK = 4096]
@@ -121,11 +122,11 @@ gqa_status make_plan(int B, int H, int G, int d, int Lmax, gqa_dtype dt, Plan *p
   if (chunk > Lmax) chunk = Lmax;
   pl->chunk = chunk;
   if (kind == KIND_MFMA) {
-    // 8 waves for d = 64 and for splits longer than 2048 positions (measured
-    // faster there), 4 otherwise; only where the head blocks fit the
-    // register budget of the larger workgroup.
+    // 4 waves (measured best on every workload with the non-temporal cache
+    // stream); 8 or 16 on request where the head blocks fit the register
+    // budget of the larger workgroup.
     const int nw_max = (pl->HB == 1 && d == 64) ? 16 : (pl->HB <= 2 ? 8 : 4);
-    const int nw_def = (d == 64 || chunk > 2048) ? 8 : 4;
+    const int nw_def = 4;
     const int nw = env_int("GQA_WAVES", nw_def);
     pl->NW = (nw == 8 || nw == 16) && nw <= nw_max ? nw : 4;
   }
@@ -252,11 +253,18 @@ gqa_status packed_impl(const void *x, const void *wp, void *const y[3], const in
   p.M = M;
   p.K = K;
   p.N = N;
-  const int nw = env_int("GQA_LINEAR_WAVES", 4) == 8 ? 8 : 4;
-  int tpi = env_int("GQA_LINEAR_TPI", 8);
-  if (tpi != 4 && tpi != 8 && tpi != 16) tpi = 8;
-  if (ceil_div(M, 16) > 2 && tpi > 8) tpi = 8;
-  const hipError_t e = gqa::launch_linear_packed(p, nw, tpi, stream);
+  // 8 waves x 2 blocks per chunk up to 512 strips, 4 x 2 beyond (measured
+  // best on the Mistral-7B projections and a 28672-wide one); GQA_LINEAR_WAVES
+  // and GQA_LINEAR_TPI override.
+  const int nw_def = N / 16 <= 512 ? 8 : 4;
+  const int nw = env_int("GQA_LINEAR_WAVES", nw_def) == 8 ? 8 : 4;
+  const int tb = ceil_div(M, 16) > 2 ? 4 : ceil_div(M, 16);
+  const int max_tpi = 32 / (tb * nw);  // two x chunks staged in LDS: TB*NW*TPI <= 32
+  int tpi = env_int("GQA_LINEAR_TPI", 2);
+  if (tpi != 1 && tpi != 2 && tpi != 4 && tpi != 8) tpi = 2;
+  if (tpi > max_tpi) tpi = max_tpi;
+  const int pd = 2;
+  const hipError_t e = gqa::launch_linear_packed(p, nw, tpi, pd, stream);
   return e == hipSuccess ? GQA_OK : hip_fail(e);
 }
 

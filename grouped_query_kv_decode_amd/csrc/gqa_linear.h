@@ -20,7 +20,7 @@ struct LinearParams {
 };
 
 hipError_t launch_linear(const LinearParams &p, int NW, int TPI, unsigned grid, hipStream_t stream);
-hipError_t launch_linear_packed(const LinearParams &p, int NW, int TPI, hipStream_t stream);
+hipError_t launch_linear_packed(const LinearParams &p, int NW, int TPI, int PD, hipStream_t stream);
 hipError_t launch_pack_weight(const void *w, void *w_packed, int K, int N, hipStream_t stream);
 
 }  // namespace gqa

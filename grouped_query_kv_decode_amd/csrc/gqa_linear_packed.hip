@@ -20,8 +20,8 @@
 // Kernel: one workgroup per 16-column strip streams the strip over all of K
 // (no split of k, so no partial sums leave the workgroup); its waves take
 // blocks in turn, TPI at a time with all loads issued before the first MFMA,
-// and are summed through LDS in wave order.  x is the B operand, read from
-// L2 (it is small and every workgroup reads all of it).
+// and are summed through LDS in wave order.  x, the B operand, is small and
+// every workgroup reads all of it (from L2), staged through LDS.
 #include "gqa_device.h"
 #include "gqa_linear.h"
 
@@ -54,7 +54,7 @@ __device__ __forceinline__ void store4(const LinearParams &p, int row, int col, 
   *reinterpret_cast<bf16x4 *>(dst) = o;
 }
 
-template <int TB, int NW, int TPI>
+template <int TB, int NW, int TPI, int PD>
 __global__ __launch_bounds__(64 * NW) void linear_packed(LinearParams p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane >> 4, nn = lane & 15;
@@ -64,29 +64,83 @@ __global__ __launch_bounds__(64 * NW) void linear_packed(LinearParams p) {
   const int nstrips = p.N / 16;
   const __bf16 *wl = p.w + (size_t)nb * 512 + lane * 8;
 
+  // x is staged through LDS a chunk of KC blocks (KC*32 values of k) at a
+  // time: read from memory as whole row segments, then each lane takes its
+  // B operand (token nn, 8 values of k) from LDS.  Read straight from memory
+  // the operand would touch 16 half-used cache lines per wave-wide load.
+  // Software pipeline: while chunk i is multiplied, x of chunk i+1 and the
+  // weights of chunks i+1 .. i+PD-1 are in flight (PD register sets for the
+  // weights, two LDS buffers for x, one barrier per chunk).
+  constexpr int KC = NW * TPI;
+  constexpr int ROWB = KC * 64 + 16;         // bytes per token row (+16: spreads the LDS banks)
+  constexpr int PPR = KC * 4;                // 16-byte pieces per row
+  constexpr int XPT = (TB * 16 * PPR + 64 * NW - 1) / (64 * NW);  // pieces per thread
+  constexpr int BUFB = TB * 16 * ROWB;
+  __shared__ __attribute__((aligned(16))) unsigned char xs[2 * BUFB];
+
   f32x4 acc[TB];
 #pragma unroll
   for (int tb = 0; tb < TB; ++tb) acc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int base = wave; base < kblocks; base += TPI * NW) {
-    u32x4 a[TPI];
-    u32x4 b[TPI][TB];
+  auto load_x = [&](u32x4 (&xr)[XPT], int kb0) {
+    const int nkb = min(KC, kblocks - kb0);
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+      const int idx = threadIdx.x + i * 64 * NW;
+      const int row = idx / PPR, pc = idx % PPR;
+      xr[i] = (row < p.M && pc < nkb * 4)
+                  ? *reinterpret_cast<const u32x4 *>(p.x + (size_t)row * p.K + kb0 * 32 + pc * 8)
+                  : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  // this wave's weight blocks of a chunk; past the end: re-read the last
+  // block (in bounds), skipped in the products
+  auto load_w = [&](u32x4 (&a)[TPI], int kb0) {
 #pragma unroll
     for (int j = 0; j < TPI; ++j) {
-      const int kb = min(base + j * NW, kblocks - 1);  // past the end: re-read the last block, skipped below
+      const int kb = min(kb0 + wave + j * NW, kblocks - 1);
       a[j] = stream_load(reinterpret_cast<const u32x4 *>(wl + (size_t)kb * nstrips * 512));
+    }
+  };
+  auto store_x = [&](const u32x4 (&xr)[XPT], unsigned char *buf) {
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+      const int idx = threadIdx.x + i * 64 * NW;
+      const int row = idx / PPR, pc = idx % PPR;
+      if (row < TB * 16) *reinterpret_cast<u32x4 *>(buf + row * ROWB + pc * 16) = xr[i];
+    }
+  };
+  auto products = [&](const u32x4 (&a)[TPI], const unsigned char *buf, int kb0) {
+    const int nkb = min(KC, kblocks - kb0);
+#pragma unroll
+    for (int j = 0; j < TPI; ++j) {
+      const int kl = wave + j * NW;  // block within the chunk
+      if (kl >= nkb) break;
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb) {
-        const int row = tb * 16 + nn;
-        b[j][tb] = row < p.M ? *reinterpret_cast<const u32x4 *>(p.x + (size_t)row * p.K + kb * 32 + 8 * c)
-                             : u32x4{0u, 0u, 0u, 0u};
+        const u32x4 b = *reinterpret_cast<const u32x4 *>(buf + (tb * 16 + nn) * ROWB + (kl * 32 + 8 * c) * 2);
+        acc[tb] = mfma(a[j], b, acc[tb]);
       }
     }
+  };
+
+  u32x4 xr[XPT], a[PD][TPI];
+  load_x(xr, 0);
 #pragma unroll
-    for (int j = 0; j < TPI; ++j) {
-      if (base + j * NW >= kblocks) break;
+  for (int d = 0; d < PD - 1; ++d)
+    if (d * KC < kblocks) load_w(a[d], d * KC);
+  int buf = 0;
+  for (int kb0 = 0; kb0 < kblocks; kb0 += PD * KC) {
 #pragma unroll
-      for (int tb = 0; tb < TB; ++tb) acc[tb] = mfma(a[j], b[j][tb], acc[tb]);
+    for (int ph = 0; ph < PD; ++ph) {
+      const int kc = kb0 + ph * KC;  // this chunk; its weights are in a[ph]
+      if (kc >= kblocks) break;
+      store_x(xr, xs + buf * BUFB);
+      if (kc + KC < kblocks) load_x(xr, kc + KC);
+      if (kc + (PD - 1) * KC < kblocks) load_w(a[(ph + PD - 1) % PD], kc + (PD - 1) * KC);
+      __syncthreads();
+      products(a[ph], xs + buf * BUFB, kc);
+      buf ^= 1;
     }
   }
 
@@ -128,38 +182,51 @@ __global__ __launch_bounds__(256) void pack_kernel(const __bf16 *__restrict__ w,
   *reinterpret_cast<u16x8 *>(wp + g * 8) = v;
 }
 
-template <int TB, int TPI>
-hipError_t launch_nw(const LinearParams &p, int NW, hipStream_t stream) {
-  const unsigned grid = (unsigned)(p.N / 16);
-  if constexpr (TB * TPI > 32) {  // does not fit the register file
+// Two x chunks in LDS, TB*16 rows of NW*TPI*64 bytes each: at most ~66 KiB.
+// PD*TPI weight operands per lane in registers.
+template <int TB, int NW, int TPI, int PD>
+hipError_t launch_one(const LinearParams &p, hipStream_t stream) {
+  if constexpr (TB * NW * TPI > 32 || PD * TPI > 16) {
     return hipErrorInvalidValue;
-  } else if (NW == 8)
-    hipLaunchKernelGGL((linear_packed<TB, 8, TPI>), dim3(grid), dim3(512), 0, stream, p);
-  else
-    hipLaunchKernelGGL((linear_packed<TB, 4, TPI>), dim3(grid), dim3(256), 0, stream, p);
-  return hipGetLastError();
+  } else {
+    hipLaunchKernelGGL((linear_packed<TB, NW, TPI, PD>), dim3(p.N / 16), dim3(64 * NW), 0, stream, p);
+    return hipGetLastError();
+  }
 }
 
-template <int TPI>
+template <int TB, int TPI, int PD>
+hipError_t launch_nw(const LinearParams &p, int NW, hipStream_t stream) {
+  return NW == 8 ? launch_one<TB, 8, TPI, PD>(p, stream) : launch_one<TB, 4, TPI, PD>(p, stream);
+}
+
+template <int TPI, int PD>
 hipError_t launch_tb(const LinearParams &p, int NW, hipStream_t stream) {
   switch ((p.M + 15) / 16) {
-    case 1: return launch_nw<1, TPI>(p, NW, stream);
-    case 2: return launch_nw<2, TPI>(p, NW, stream);
+    case 1: return launch_nw<1, TPI, PD>(p, NW, stream);
+    case 2: return launch_nw<2, TPI, PD>(p, NW, stream);
     case 3:
-    case 4: return launch_nw<4, TPI>(p, NW, stream);
+    case 4: return launch_nw<4, TPI, PD>(p, NW, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int PD>
+hipError_t launch_tpi(const LinearParams &p, int NW, int TPI, hipStream_t stream) {
+  switch (TPI) {
+    case 1: return launch_tb<1, PD>(p, NW, stream);
+    case 2: return launch_tb<2, PD>(p, NW, stream);
+    case 4: return launch_tb<4, PD>(p, NW, stream);
+    case 8: return launch_tb<8, PD>(p, NW, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-hipError_t launch_linear_packed(const LinearParams &p, int NW, int TPI, hipStream_t stream) {
-  switch (TPI) {
-    case 4: return launch_tb<4>(p, NW, stream);
-    case 8: return launch_tb<8>(p, NW, stream);
-    case 16: return launch_tb<16>(p, NW, stream);
-    default: return hipErrorInvalidValue;
-  }
+hipError_t launch_linear_packed(const LinearParams &p, int NW, int TPI, int PD, hipStream_t stream) {
+  // prefetch distance 2 (one chunk ahead) measured best; deeper rings are
+  // available to the template but not instantiated
+  return PD == 2 ? launch_tpi<2>(p, NW, TPI, stream) : hipErrorInvalidValue;
 }
 
 hipError_t launch_pack_weight(const void *w, void *w_packed, int K, int N, hipStream_t stream) {
