@@ -73,10 +73,11 @@ gqa_status check_shape(int B, int H, int G, int d, int Lmax, gqa_dtype dt) {
 //    spreads a group's head blocks over 2 or 4 workgroups (GQA_HEAD_SPLIT).
 //  - splits: one workgroup per (b, g, head chunk, split).  The split length
 //    is chosen so that the grid holds about GQA_TARGET_WGS = 256 workgroups
-//    (one per compute unit), clamped to [512, GQA_MAX_CHUNK = 4096]
-//    positions: long splits amortise each workgroup's prologue and epilogue,
-//    the cap keeps ragged batches balanced.  Half the compute units cannot
-//    keep HBM busy, so a shape with fewer (b, g) units than that is split.
+//    (one per compute unit), at least 256 positions (matrix cores) or 32
+//    (VALU), at least Lmax/32, at most GQA_MAX_CHUNK = 4096: long splits
+//    amortise each workgroup's prologue and epilogue, the cap keeps ragged
+//    batches balanced.  Half the compute units cannot keep HBM busy, so a
+//    shape with fewer (b, g) units than that is split.
 //  - when a sequence spans several splits, the workgroup that finishes its
 //    (b, g) unit last merges the partials inside the same kernel; with more
 //    units than counters (or GQA_MERGE=kernel) a second kernel merges instead.
@@ -116,7 +117,14 @@ gqa_status make_plan(int B, int H, int G, int d, int Lmax, gqa_dtype dt, Plan *p
     long S = (target + units - 1) / units;
     if (S < 1) S = 1;
     chunk = (int)round_up((size_t)ceil_div(Lmax, S), 32);
-    if (chunk < 512) chunk = 512;
+    // Floors: the matrix-core kernel's 4 waves take 8 tiles of 32 positions
+    // per 256 (shorter splits cost more in epilogue and merge than they
+    // gain), the VALU kernel's rows are shorter; and at most 32 splits per
+    // sequence, which bounds the merge.
+    const int min_chunk = kind == KIND_MFMA ? 256 : 32;
+    if (chunk < min_chunk) chunk = min_chunk;
+    const int min_for_merge = (int)round_up((size_t)ceil_div(Lmax, 32), 32);
+    if (chunk < min_for_merge) chunk = min_for_merge;
     if (chunk > max_chunk) chunk = max_chunk;
   }
   if (chunk > Lmax) chunk = Lmax;

@@ -106,6 +106,32 @@ def test_workspace_size_model(lib, monkeypatch):
     assert lib.gqa_decode_workspace_size(B, 6, 4, d, L, BF16) == 0  # rejected shape
 
 
+def _decode_ws(B, H, S, d):
+    return 256 * 1024 + (B * H * S * 8 + 255) // 256 * 256 + B * H * S * d * 4
+
+
+def test_split_plan_model(lib, monkeypatch):
+    """Split lengths: about 256 workgroups, at least 256 positions on the
+    matrix cores (32 on the VALU kernel), at least Lmax/32, at most 4096."""
+    for k in ("GQA_CHUNK", "GQA_TARGET_WGS", "GQA_MAX_CHUNK", "GQA_KERNEL", "GQA_HEAD_SPLIT", "GQA_MERGE"):
+        monkeypatch.delenv(k, raising=False)
+    cases = [
+        # (B, H, G, d, L, dtype, splits)
+        (16, 32, 8, 128, 4096, BF16, 2),      # 128 units: 2048-position splits
+        (1, 32, 8, 128, 4096, BF16, 16),      # 8 units: 256-position floor
+        (4, 32, 8, 128, 4096, BF16, 8),       # 32 units: 512
+        (1, 32, 8, 128, 32768, BF16, 32),     # 8 units, long: 1024 (256 WGs)
+        (64, 64, 8, 128, 32768, BF16, 8),     # 512 units: 4096 cap
+        (8, 32, 16, 128, 8192, BF16, 2),      # 128 units: 4096
+        (1, 8, 2, 64, 256, F32, 8),           # VALU, 2 units: 32-position floor
+        (1, 8, 2, 64, 8192, F32, 32),         # VALU: at most 32 splits
+    ]
+    for B, H, G, d, L, dt, S in cases:
+        assert lib.gqa_decode_workspace_size(B, H, G, d, L, dt) == _decode_ws(B, H, S, d), (B, H, G, d, L, dt, S)
+    # one split: no workspace
+    assert lib.gqa_decode_workspace_size(32, 64, 8, 64, 2048, BF16) == 0
+
+
 def test_kernel_selection(lib, monkeypatch):
     monkeypatch.delenv("GQA_KERNEL", raising=False)
     assert lib.gqa_decode_kernel_kind(16, 32, 8, 128, 4096, BF16) == 1

@@ -99,7 +99,7 @@ SMALL = [
 @pytest.mark.parametrize("case", SMALL, ids=lambda c: "B%d_H%d_G%d_d%d_L%d" % c[:5])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("kernel", ["default", "valu"])
-@pytest.mark.parametrize("chunk", [None, 128, 100000])
+@pytest.mark.parametrize("chunk", [None, 32, 128, 100000])
 @pytest.mark.parametrize("merge", ["fused", "kernel"])
 def test_small_parity(env, case, dtype, kernel, chunk, merge):
     B, H, G, d, L, lens = case
