@@ -364,8 +364,8 @@ def decode_layer_workspace_size(B, H, G, d, Lmax, window, d_model, dtype) -> int
 
 class LayerStep:
     """The full decode step (projections, cache append, attention, output
-    projection; gqa_decode_layer) bound to fixed tensors and to the stream
-    current at construction.  w_qkv [d_model, (H+2G)d] and w_o [H d, d_model]
+    projection; gqa_decode_layer) bound to fixed tensors; each call runs on
+    torch's current stream.  w_qkv [d_model, (H+2G)d] and w_o [H d, d_model]
     are row-major; they are packed once here (pack_weight)."""
 
     def __init__(self, x, w_qkv, w_o, k_cache, v_cache, seq_lens, H: int, G: int, scale: float, window: int = 0,
@@ -398,10 +398,13 @@ class LayerStep:
         self._args = (x.data_ptr(), self.w_qkv_packed.data_ptr(), self.w_o_packed.data_ptr(), k_cache.data_ptr(),
                       v_cache.data_ptr(),
                       seq_lens.data_ptr(), B, H, G, d, Lmax, int(window), d_model, float(scale), GQA_BF16,
-                      out.data_ptr(), ws_ptr, ws_bytes, _stream_handle(x.device))
+                      out.data_ptr(), ws_ptr, ws_bytes)
+        self._device = x.device
 
     def __call__(self):
-        st = self._fn(*self._args)
+        """One step, enqueued on torch's current stream (so it can be
+        captured into a graph)."""
+        st = self._fn(*self._args, _stream_handle(self._device))
         if st:
             raise GQAError(st, "gqa_decode_layer")
         return self.out
