@@ -101,6 +101,11 @@ def cpu_baseline(w, q, k, v, lens, out_gpu, budget_s: float):
             ref = np.stack(outs)
         if elapsed >= budget_s or reps >= 1000:
             break
+    # single-thread reference: one sequence of the batch, scaled to the batch
+    qq, kk, vv, ll = seqs[0]
+    t0 = time.perf_counter()
+    ora.decode(qq, kk, vv, ll, w.scale, nthreads=1)
+    t_one = time.perf_counter() - t0
     got = out_gpu.float().cpu().double().numpy()
     err = float(np.max(np.abs(got - ref)))
     tol = 1e-5 if w.dtype == "f32" else 2e-2
@@ -109,6 +114,7 @@ def cpu_baseline(w, q, k, v, lens, out_gpu, budget_s: float):
         "sample": "%d full batch(es) of the workload (%d sequences each), binary64 C oracle, %d threads over "
                   "(sequence, head); host copy %.2f s excluded" % (reps, w.B, threads, t_copy),
         "seconds_per_batch": elapsed / reps,
+        "single_thread_seconds_per_batch": t_one * w.B if not w.ragged else None,
     }
     parity = {"max_abs_err": err, "tol": tol, "pass": bool(err <= tol and np.isfinite(got).all())}
     return base, parity

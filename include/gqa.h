@@ -99,11 +99,14 @@ gqa_status gqa_workspace_init(void *workspace, size_t workspace_bytes, hipStream
  *   stream    HIP stream the work is enqueued on (NULL: the null stream).
  *
  * Enqueues one kernel: a workgroup per (sequence, K/V head, context split)
- * streams that part of the cache once for all query heads of the group; when
- * a sequence spans several splits, the workgroup that finishes its (sequence,
- * K/V head) last merges the split results (log-sum-exp) into out.  Above
- * 65536 (sequence, K/V head) units, or with the environment variable
- * GQA_MERGE=kernel, a second kernel does that merge instead.
+ * streams that part of the cache once for all query heads of the group (with
+ * few (sequence, K/V head) units, the group's heads are spread over 2 or 4
+ * workgroups that read the same part); when a sequence spans several splits,
+ * the workgroup that finishes its unit last merges the split results
+ * (log-sum-exp) into out.  Above 65536 units, or with the environment
+ * variable GQA_MERGE=kernel, a second kernel does that merge instead.  The
+ * call allocates nothing, does not synchronise and issues no memset, so it
+ * can be captured into a HIP graph (with a workspace cleared beforehand).
  * NaN or Inf inside the attended positions propagate to the output.
  */
 gqa_status gqa_decode(const void *q, const void *k_cache, const void *v_cache, const int32_t *seq_lens,
