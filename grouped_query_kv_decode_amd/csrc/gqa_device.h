@@ -158,7 +158,7 @@ __device__ __forceinline__ bool arrive_last(unsigned *counter, int nsplit) {
 // the separate merge kernel calls this same routine.
 template <typename T, int D>
 __device__ void merge_heads(const DecodeParams &p, int b, int head0, int nh, int nsplit) {
-  constexpr int kBatch = 8;
+  constexpr int kBatch = 16;
   for (int idx = threadIdx.x; idx < nh * (D / 4); idx += blockDim.x) {
     const int j = idx / (D / 4), c = (idx % (D / 4)) * 4;
     const size_t hs = ((size_t)b * p.H + head0 + j) * p.S;
