@@ -11,6 +11,7 @@ HIP events on the launch stream, against 8 TB/s), and the CPU oracle timed on
 a bounded sample of the same workload.
 
 Other modes (used to produce the files under profiles/):
+    --meanpool                 the mean-pool conversion step (one JSON line)
     --calibrate-copy           plain device copy of a known size, for scaling
                                the FETCH_SIZE / WRITE_SIZE counters
     --summarize-rocprof DIR    print a summary of rocprofv3 CSV output
@@ -286,6 +287,43 @@ def calibrate_copy(args):
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "calls": args.steps}), flush=True)
 
 
+def meanpool_bench(args):
+    """The conversion step (mean-pool of the K or V projection within each
+    group) on the Mistral-7B shapes: W [4096, 32*128] binary32 -> [4096, 8*128].
+    One JSON line: time per call, algorithmic bytes (read W once, write the
+    result once) / time against 8 TB/s, and a bit-exact check against the
+    oracle on the last call's result."""
+    import numpy as np
+    import torch
+    import grouped_query_kv_decode_amd as gqa
+    sys.path.insert(0, ROOT)
+    import oracle
+    dev = torch.device("cuda:0")
+    d_model, H, G, h = 4096, 32, 8, 128
+    gen = torch.Generator(dev).manual_seed(1234)
+    rot = 8  # 8 x 64 MiB inputs: beyond the 256 MB Infinity Cache
+    ws = [torch.randn((d_model, H * h), generator=gen, device=dev) for _ in range(rot)]
+    out = torch.empty((d_model, G * h), dtype=torch.float32, device=dev)
+    for i in range(args.warmup):
+        gqa.meanpool_kv(ws[i % rot], H, G, out=out)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        gqa.meanpool_kv(ws[i % rot], H, G, out=out)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / args.steps
+    last = (args.steps - 1) % rot
+    ref = oracle.meanpool(ws[last].cpu().numpy(), H, G)
+    exact = bool(np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32)))
+    ab = d_model * H * h * 4 + d_model * G * h * 4
+    print(json.dumps({"mode": "meanpool", "d_model": d_model, "H": H, "G": G, "h": h, "dtype": "f32",
+                      "us_per_call": us, "alg_bytes": ab, "alg_GBps": ab / us / 1e3,
+                      "frac_of_8TBps": ab / us / 8e6, "bit_exact_vs_oracle": exact, "steps": args.steps}), flush=True)
+
+
 def counter_mean(d, counter, kernel_substr):
     """Mean per-dispatch value of a rocprofv3 --pmc counter for kernels whose name contains kernel_substr."""
     vals = [float(r["Counter_Value"]) for r in _read_csvs(d, "counter_collection.csv")
@@ -361,6 +399,7 @@ def main():
     ap.add_argument("--window", type=int, default=4096, help="window for --variant window/append (0: none)")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time to aim for")
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--meanpool", action="store_true", help="time the K/V mean-pool conversion step")
     ap.add_argument("--fig6", action="store_true", help="the pages' fig. 6 group sweep as decoder attention")
     ap.add_argument("--fig6-batch", type=int, default=32)
     ap.add_argument("--summarize-rocprof", metavar="DIR")
@@ -382,6 +421,9 @@ def main():
         print("bench.py measures one GPU: this build has no multi-GPU path (collectives and sharding are out of "
               "scope); run with --gpus 1", file=sys.stderr)
         return 2
+    if args.meanpool:
+        meanpool_bench(args)
+        return 0
     if args.calibrate_copy:
         calibrate_copy(args)
         return 0
