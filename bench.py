@@ -290,14 +290,11 @@ def calibrate_copy(args):
 def meanpool_bench(args):
     """The conversion step (mean-pool of the K or V projection within each
     group) on the Mistral-7B shapes: W [4096, 32*128] binary32 -> [4096, 8*128].
-    One JSON line: time per call, algorithmic bytes (read W once, write the
-    result once) / time against 8 TB/s, and a bit-exact check against the
-    oracle on the last call's result."""
-    import numpy as np
+    One JSON line: time per call and algorithmic bytes (read W once, write the
+    result once) / time against 8 TB/s.  (Bit-exactness against the oracle is
+    checked by the GPU tests.)"""
     import torch
     import grouped_query_kv_decode_amd as gqa
-    sys.path.insert(0, ROOT)
-    import oracle
     dev = torch.device("cuda:0")
     d_model, H, G, h = 4096, 32, 8, 128
     gen = torch.Generator(dev).manual_seed(1234)
@@ -315,13 +312,10 @@ def meanpool_bench(args):
     e1.record(stream)
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / args.steps
-    last = (args.steps - 1) % rot
-    ref = oracle.meanpool(ws[last].cpu().numpy(), H, G)
-    exact = bool(np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32)))
     ab = d_model * H * h * 4 + d_model * G * h * 4
     print(json.dumps({"mode": "meanpool", "d_model": d_model, "H": H, "G": G, "h": h, "dtype": "f32",
                       "us_per_call": us, "alg_bytes": ab, "alg_GBps": ab / us / 1e3,
-                      "frac_of_8TBps": ab / us / 8e6, "bit_exact_vs_oracle": exact, "steps": args.steps}), flush=True)
+                      "frac_of_8TBps": ab / us / 8e6, "steps": args.steps}), flush=True)
 
 
 def counter_mean(d, counter, kernel_substr):
