@@ -329,3 +329,32 @@ def test_layer_step_reuse(ksplit):
         assert torch.equal(y1, y2), t
         lens += 1
     assert torch.equal(k.view(torch.int16), k2.view(torch.int16))
+
+
+# --------------------------------------------------------------- seeded random shapes
+
+def _random_linear(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        M = int(rng.integers(1, 65))
+        K = 32 * int(rng.integers(1, 97))
+        N = 16 * int(rng.integers(1, 161))
+        out.append((i, M, K, N))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_linear(24, 77), ids=lambda c: "rand%02d_M%d_K%d_N%d" % c)
+def test_random_projections(ksplit, case):
+    """gqa_linear_packed on random (M, K, N); gqa_linear as well where N is a
+    multiple of 128."""
+    i, M, K, N = case
+    x = rand_bf16((M, K), seed=9000 + i)
+    w = rand_bf16((K, N), seed=9100 + i, std=K ** -0.5)
+    y = gqa.linear_packed(x.to(DEV), gqa.pack_weight(w.to(DEV)), N)
+    torch.cuda.synchronize()
+    check_linear(y, x, w, "packed rand%02d M%d K%d N%d" % case)
+    if N % 128 == 0:
+        y2 = gqa.linear(x.to(DEV), w.to(DEV))
+        torch.cuda.synchronize()
+        check_linear(y2, x, w, "row-major rand%02d M%d K%d N%d" % case)

@@ -424,3 +424,56 @@ def test_meanpool_bit_exact(shape):
     torch.cuda.synchronize()
     ref = oracle.meanpool(w.numpy(), H, G)
     assert np.array_equal(got.numpy().view(np.uint32), ref.view(np.uint32))
+
+
+# --------------------------------------------------------------- seeded random configurations
+
+def _random_cases(n, seed):
+    """Small random shapes across the plan space: group ratios 1..64 (head
+    splits, padded head blocks), lengths that are not multiples of 32 (tails,
+    empty sequences), windows, the cache append, both dtypes."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        d = int(rng.choice([64, 128]))
+        G = int(rng.choice([1, 2, 3, 4, 8]))
+        r = int(rng.choice([1, 2, 3, 4, 5, 7, 8, 12, 16, 24, 40, 48, 64]))
+        B = int(rng.integers(1, 6))
+        Lmax = int(rng.integers(1, 1400))
+        lens = [int(x) for x in rng.integers(0, Lmax + 1, size=B)]
+        lens[0] = Lmax  # one full sequence
+        dtype = "bf16" if rng.random() < 0.75 else "f32"
+        window = int(rng.integers(1, Lmax + 40)) if rng.random() < 0.3 else 0
+        append = bool(rng.random() < 0.3)
+        merge = "kernel" if rng.random() < 0.2 else None
+        cases.append((i, B, G * r, G, d, Lmax, lens, dtype, window, append, merge))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_cases(48, 2026), ids=lambda c: "rand%02d" % c[0])
+def test_random_configurations(env, case):
+    i, B, H, G, d, Lmax, lens, dtype, window, append, merge = case
+    env(GQA_MERGE=merge)
+    q, k, v, lt, scale = rand_case(B, H, G, d, Lmax, lens, dtype, seed=5000 + i)
+    what = "rand%02d B%d H%d G%d d%d L%d %s W%d append=%s merge=%s" % (i, B, H, G, d, Lmax, dtype, window, append,
+                                                                       merge)
+    if append:
+        gen = torch.Generator(DEV).manual_seed(6000 + i)
+        kn = torch.randn((B, G, d), generator=gen, device=DEV).to(k.dtype)
+        vn = torch.randn((B, G, d), generator=gen, device=DEV).to(k.dtype)
+        k0, v0 = k.cpu(), v.cpu()
+        out = gqa.decode_append(q, kn, vn, k, v, lt, scale, window=window)
+        torch.cuda.synchronize()
+        ref, rk, rv = oracle.decode_append(q.cpu(), kn.cpu(), vn.cpu(), k0, v0, lt.cpu(), scale, window=window)
+        check(out, ref, dtype, what)
+        bits = torch.int16 if dtype == "bf16" else torch.int32
+        nbits = np.uint16 if dtype == "bf16" else np.uint32
+        assert np.array_equal(k.cpu().view(bits).numpy().view(nbits), rk.view(nbits)), what
+        assert np.array_equal(v.cpu().view(bits).numpy().view(nbits), rv.view(nbits)), what
+    elif window:
+        out = gqa.decode_window(q, k, v, lt, scale, window)
+        torch.cuda.synchronize()
+        check(out, oracle.decode(q.cpu(), k.cpu(), v.cpu(), lt.cpu(), scale, window=window), dtype, what)
+    else:
+        out = run_gpu(q, k, v, lt, scale)
+        check(out, oracle_out(q, k, v, lt, scale), dtype, what)
