@@ -245,6 +245,7 @@ gqa_status check_layer(int B, int H, int G, int d, int Lmax, int window, int d_m
   gqa_status st = check_shape(B, H, G, d, Lmax, dtype);
   if (st != GQA_OK) return st;
   if (window < 0 || d_model < 1) return GQA_ERR_SHAPE;
+  if ((long long)(H + 2LL * G) * d > 0x7fffffffLL) return GQA_ERR_SIZE;
   st = check_packed(B, d_model, (H + 2 * G) * d, dtype);
   if (st == GQA_OK) st = check_packed(B, H * d, d_model, dtype);
   return st;

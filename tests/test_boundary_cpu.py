@@ -275,6 +275,7 @@ def test_decode_layer_arguments(lib):
     assert layer(H=7) == SHAPE
     assert layer(W=-1) == SHAPE
     assert layer(dm=0) == SHAPE
+    assert layer(H=1 << 24, G=1 << 22) == SIZE  # (H + 2G) d beyond the int range
     assert layer(B=0, x=None, ws=None) == OK
     assert layer(x=None) == NULL
     assert layer(ws=None) == NULL
