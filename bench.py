@@ -35,10 +35,17 @@ KERNEL_SOURCES = ["gqa_device.h", "gqa_decode_mfma.hip", "gqa_decode_valu.hip"]
 
 
 def kernel_source_hash() -> str:
+    """Hash of the decode kernels' code (comments and blank lines removed, so
+    that editing documentation does not invalidate measured counters)."""
+    import re
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "grouped_query_kv_decode_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "grouped_query_kv_decode_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        lines = [l.rstrip() for l in text.splitlines() if l.strip()]
+        h.update("\n".join(lines).encode())
     return h.hexdigest()[:16]
 
 

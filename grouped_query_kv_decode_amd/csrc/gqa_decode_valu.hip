@@ -1,8 +1,9 @@
 // Grouped-query decode attention on the vector ALUs (binary32 and bfloat16).
 //
 // One workgroup (4 waves) owns (sequence b, K/V head g, head chunk hc, split
-// s): it streams positions [s*chunk, min((s+1)*chunk, len_b)) of K/V head g
-// once and serves up to RC query heads of the group from every row it loads
+// s): it streams positions [lo + s*chunk, min(lo + (s+1)*chunk, len_b)) of
+// K/V head g once (lo = 0, or the first position of the sliding window) and
+// serves up to RC query heads of the group from every row it loads
 // (wikillm "Grouped-query attention (GQA)", Overview: every query head of a
 // group attends with the group's single key and value head).
 //
