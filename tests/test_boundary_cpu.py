@@ -107,12 +107,19 @@ def test_workspace_size_model(lib, monkeypatch):
 
 
 def _decode_ws(B, H, S, d):
-    return 256 * 1024 + (B * H * S * 8 + 255) // 256 * 256 + B * H * S * d * 4
+    """Counters, split (max, sum) and outputs; with more than 32 splits also
+    the results of the split groups (16 splits each)."""
+    up = lambda x: (x + 255) // 256 * 256
+    ws = 256 * 1024 + up(B * H * S * 8) + B * H * S * d * 4
+    if S > 32:
+        ng = (S + 15) // 16
+        ws = 256 * 1024 + up(B * H * S * 8) + up(B * H * S * d * 4) + up(B * H * ng * 8) + B * H * ng * d * 4
+    return ws
 
 
 def test_split_plan_model(lib, monkeypatch):
     """Split lengths: about 256 workgroups, at least 256 positions on the
-    matrix cores (32 on the VALU kernel), at least Lmax/32, at most 4096."""
+    matrix cores (32 on the VALU kernel), at least Lmax/256, at most 4096."""
     for k in ("GQA_CHUNK", "GQA_TARGET_WGS", "GQA_MAX_CHUNK", "GQA_KERNEL", "GQA_HEAD_SPLIT", "GQA_MERGE"):
         monkeypatch.delenv(k, raising=False)
     cases = [
@@ -124,7 +131,9 @@ def test_split_plan_model(lib, monkeypatch):
         (64, 64, 8, 128, 32768, BF16, 8),     # 512 units: 4096 cap
         (8, 32, 16, 128, 8192, BF16, 2),      # 128 units: 4096
         (1, 8, 2, 64, 256, F32, 8),           # VALU, 2 units: 32-position floor
-        (1, 8, 2, 64, 8192, F32, 32),         # VALU: at most 32 splits
+        (1, 8, 2, 64, 8192, F32, 128),        # VALU, 2 units: 64-position splits
+        (1, 8, 1, 128, 131072, BF16, 256),    # one unit, long: 512-position splits (256 WGs)
+        (1, 8, 1, 128, 262144, F32, 256),     # at most 256 splits: 1024 positions
     ]
     for B, H, G, d, L, dt, S in cases:
         assert lib.gqa_decode_workspace_size(B, H, G, d, L, dt) == _decode_ws(B, H, S, d), (B, H, G, d, L, dt, S)

@@ -110,6 +110,62 @@ def test_small_parity(env, case, dtype, kernel, chunk, merge):
     check(out, oracle_out(q, k, v, lens_t, scale), dtype, "%s %s chunk=%s %s" % (dtype, kernel, chunk, case))
 
 
+# Many splits per sequence: beyond 32 the in-kernel merge has two levels
+# (the last of each group of 16 splits folds the group, the last group folds
+# the groups).  Units with one group, several groups and a partial last group
+# side by side.
+MANY_SPLITS = [
+    # (B, H, G, d, Lmax, lens, chunk)
+    (3, 32, 8, 128, 9000, [9000, 4100, 300], 256),     # 36 splits (16 + 16 + 4), 17, 2
+    (2, 8, 1, 128, 20000, [20000, 16 * 256 + 1], 256),  # r = 8: 79 splits; 17
+    (2, 64, 1, 64, 12000, [12000, 5000], 256),         # head chunks: 47 and 20 splits
+    (1, 8, 2, 64, 8192, [8192], 32),                    # 256 splits, the planner's maximum
+]
+
+
+@pytest.mark.parametrize("case", MANY_SPLITS, ids=lambda c: "B%d_H%d_G%d_d%d_L%d_c%d" % (c[:5] + (c[6],)))
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("kernel", ["default", "valu"])
+@pytest.mark.parametrize("merge", ["fused", "kernel"])
+def test_many_splits(env, case, dtype, kernel, merge):
+    B, H, G, d, L, lens, chunk = case
+    env(GQA_KERNEL=None if kernel == "default" else kernel, GQA_CHUNK=chunk,
+        GQA_MERGE=None if merge == "fused" else "kernel")
+    q, k, v, lens_t, scale = rand_case(B, H, G, d, L, lens, dtype, seed=sum(case[:5]) + chunk)
+    out = run_gpu(q, k, v, lens_t, scale)
+    check(out, oracle_out(q, k, v, lens_t, scale), dtype, "%s %s %s %s" % (dtype, kernel, merge, case))
+
+
+def test_many_splits_window_and_append(env):
+    """Sliding window and cache append with more than 32 splits per sequence."""
+    env(GQA_CHUNK=256)
+    B, H, G, d, L = 2, 32, 8, 128, 9000
+    lens = [9000, 6100]
+    q, k, v, lt, scale = rand_case(B, H, G, d, L, lens, "bf16", seed=31)
+    gen = torch.Generator(DEV).manual_seed(32)
+    kn = torch.randn((B, G, d), generator=gen, device=DEV).to(torch.bfloat16)
+    vn = torch.randn((B, G, d), generator=gen, device=DEV).to(torch.bfloat16)
+    out_w = gqa.decode_window(q, k, v, lt, scale, window=5000)
+    torch.cuda.synchronize()
+    check(out_w, oracle.decode(q.cpu(), k.cpu(), v.cpu(), lt.cpu(), scale, window=5000), "bf16", "window 5000")
+    k0, v0 = k.cpu(), v.cpu()
+    out = gqa.decode_append(q, kn, vn, k, v, lt, scale)
+    torch.cuda.synchronize()
+    ref, rk, rv = oracle.decode_append(q.cpu(), kn.cpu(), vn.cpu(), k0, v0, lt.cpu(), scale)
+    check(out, ref, "bf16", "append, many splits")
+    assert np.array_equal(k.cpu().view(torch.int16).numpy().view(np.uint16), rk.view(np.uint16))
+    assert np.array_equal(v.cpu().view(torch.int16).numpy().view(np.uint16), rv.view(np.uint16))
+
+
+def test_long_single_sequence(env):
+    """One sequence, one K/V head, 131072 positions: the planner's 256 splits
+    of 512 positions (every compute unit busy), two-level merge."""
+    w = wl.Workload("long", 1, 8, 1, 128, 131072, "bf16", 41)
+    q, k, v, lens = wl.make_inputs(w, DEV)
+    out = run_gpu(q, k, v, lens, w.scale)
+    check(out, oracle_out(q, k, v, lens, w.scale), "bf16", "B1 H8 G1 d128 L131072")
+
+
 def test_tiny_workload_fp32(env):
     w = wl.TINY_F32
     q, k, v, lens = wl.make_inputs(w, DEV)
@@ -272,7 +328,8 @@ def test_fused_merge_matches_merge_kernel(env, kernel):
     call after call, on shapes with many concurrent splits."""
     cases = [rand_case(16, 32, 8, 128, 4096, [4096] * 16, "bf16", seed=21),
              rand_case(32, 64, 8, 64, 2048, [2048 - 37 * i for i in range(32)], "bf16", seed=22),
-             rand_case(4, 16, 4, 128, 3000, [3000, 1, 1500, 2999], "f32", seed=23)]
+             rand_case(4, 16, 4, 128, 3000, [3000, 1, 1500, 2999], "f32", seed=23),
+             rand_case(3, 32, 8, 128, 9000, [9000, 4100, 300], "bf16", seed=24)]  # 36 splits: two levels
     for q, k, v, lens, scale in cases:
         env(GQA_KERNEL=None if kernel == "default" else kernel, GQA_CHUNK=256, GQA_MERGE="kernel")
         ref = run_gpu(q, k, v, lens, scale).clone()
