@@ -11,6 +11,11 @@ HIP events on the launch stream, against 8 TB/s), and the CPU oracle timed on
 a bounded sample of the same workload.
 
 Other modes (used to produce the files under profiles/):
+    --variant append|window|layer   decode with the cache append, sliding-window
+                               decode, the whole decode step of a layer
+    --fig6                     the pages' fig. 6 group sweep as decoder attention
+    --shapes                   serving shapes: batch 1..256, context 1K..128K
+                               (one JSON line per shape)
     --meanpool                 the mean-pool conversion step (one JSON line)
     --calibrate-copy           plain device copy of a known size, for scaling
                                the FETCH_SIZE / WRITE_SIZE counters
@@ -325,6 +330,56 @@ def meanpool_bench(args):
                       "frac_of_8TBps": ab / us / 8e6, "steps": args.steps}), flush=True)
 
 
+# Serving shapes beyond the named workloads (bfloat16, full-length caches):
+# (H, G, d) of common models - 32/8/128 Llama-3-8B-like, 8/1/128 one GPU's
+# share of a 64-query-head, 8-K/V-head model split 8 ways, 32/16/128 Gemma-2-
+# like, 64/4/128 a wide group, 16/8/64 - at batch 1 .. 256, contexts 1K .. 128K.
+SERVING_HEADS = [(32, 8, 128), (8, 1, 128), (32, 16, 128), (64, 4, 128), (16, 8, 64)]
+SERVING_BL = [(1, 1024), (1, 32768), (1, 131072), (4, 8192), (16, 1024), (64, 2048), (64, 8192), (256, 1024),
+              (256, 4096)]
+
+
+def shapes_bench(args):
+    """One JSON line per serving shape: time per gqa_decode call (HIP events
+    over back-to-back calls, inputs rotated through >= 1 GiB where memory
+    allows) and algorithmic bytes / time against 8 TB/s."""
+    import torch
+    import grouped_query_kv_decode_amd as gqa
+    from grouped_query_kv_decode_amd import workloads as wl
+    dev = torch.device("cuda:0")
+    gqa.load_library()
+    stream = torch.cuda.current_stream()
+    for (H, G, d) in SERVING_HEADS:
+        for (B, L) in SERVING_BL:
+            kvb = 2 * B * G * L * d * 2
+            if kvb > (8 << 30):
+                continue
+            w = wl.Workload("serving_B%d_H%d_G%d_d%d_L%d" % (B, H, G, d, L), B, H, G, d, L, "bf16", 5)
+            rot = min(16, max(2, (1 << 30) // kvb))
+            sets = [wl.make_inputs(w, dev, pad="none", seed_offset=i) for i in range(rot)]
+            decs = [gqa.Decoder(q, k, v, lens, w.scale) for (q, k, v, lens) in sets]
+            ab = kvb + 2 * B * H * d * 2
+            for i in range(10):
+                decs[i % rot]()
+            n = max(20, min(400, int(2e5 / max(1.0, ab / 7e6))))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for i in range(n):
+                decs[i % rot]()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / n
+            kind = gqa.decode_kernel_kind(B, H, G, d, L, gqa.GQA_BF16)
+            splits = gqa.decode_workspace_size(B, H, G, d, L, gqa.GQA_BF16) > 0
+            print(json.dumps({"mode": "shapes", "B": B, "H": H, "G": G, "d": d, "Lmax": L, "dtype": "bf16",
+                              "kernel": ["valu", "mfma"][kind], "split": splits, "steps": n, "rotation_sets": rot,
+                              "us_per_call": us, "alg_bytes": ab, "alg_GBps": ab / us / 1e3,
+                              "frac_of_8TBps": ab / us / 8e6}), flush=True)
+            del sets, decs
+            torch.cuda.empty_cache()
+
+
 def counter_mean(d, counter, kernel_substr):
     """Mean per-dispatch value of a rocprofv3 --pmc counter for kernels whose name contains kernel_substr."""
     vals = [float(r["Counter_Value"]) for r in _read_csvs(d, "counter_collection.csv")
@@ -403,6 +458,7 @@ def main():
     ap.add_argument("--meanpool", action="store_true", help="time the K/V mean-pool conversion step")
     ap.add_argument("--fig6", action="store_true", help="the pages' fig. 6 group sweep as decoder attention")
     ap.add_argument("--fig6-batch", type=int, default=32)
+    ap.add_argument("--shapes", action="store_true", help="serving shapes sweep (batch 1..256, context 1K..128K)")
     ap.add_argument("--summarize-rocprof", metavar="DIR")
     ap.add_argument("--write-traffic", action="store_true",
                     help="combine counter runs (--fetch-dir, --write-dir, --copy-fetch-dir, --copy-write-dir)")
@@ -430,6 +486,9 @@ def main():
         return 0
     if args.fig6:
         fig6(args)
+        return 0
+    if args.shapes:
+        shapes_bench(args)
         return 0
     run_bench(args)
     return 0

@@ -38,28 +38,24 @@ int next_pow2(int x) {
 enum { KIND_VALU = 0, KIND_MFMA = 1 };
 
 // Workspace layout when some sequence may span several splits:
-//   [0, kCounterBytes)  arrival counters: one per (b, g, head chunk) unit,
-//                       then, with more than kOneLevel splits, NG per unit
-//                       for the split groups; zero between calls (each call
-//                       leaves them zero)
-//   ml region           float2 [B, H, S]    split (max, weight sum)
+//   [0, kCounterBytes)  arrival counters, one per (b, g, head chunk) unit;
+//                       zero between calls (each call leaves them zero)
+//   ml region           float2 [B, H, S]   split (max, weight sum)
 //   o region            float  [B, H, S, d] split un-normalised outputs
-//   ml1, o1 regions     float2 [B, H, NG], float [B, H, NG, d]: group results
-//                       (only when S > kOneLevel)
 // The counter region is never used for anything else, whatever the shape,
 // so one cleared workspace serves calls of any shape.
 constexpr size_t kCounterBytes = 256 * 1024;
 constexpr long kMaxFusedUnits = kCounterBytes / sizeof(unsigned);  // counters
-constexpr int kMaxSplits = 256;  // splits per sequence the planner uses at most
+constexpr int kMaxSplits = 256;     // splits per sequence the planner uses at most
+constexpr int kMaxFusedSplits = 32; // more splits: merged by the wide merge kernel
 
 struct Plan {
   int kind;
   int chunk, S, HC, RC, HB;
   int NW;  // waves per workgroup (matrix-core kernel)
   int fused;
-  int NG;  // split groups per unit (two-level merge), 0 when S <= kOneLevel
   unsigned grid;
-  size_t ml_off, o_off, ml1_off, o1_off, ws_bytes;
+  size_t ml_off, o_off, ws_bytes;
 };
 
 gqa_status check_shape(int B, int H, int G, int d, int Lmax, gqa_dtype dt) {
@@ -126,7 +122,7 @@ gqa_status make_plan(int B, int H, int G, int d, int Lmax, gqa_dtype dt, Plan *p
     // Floors: the matrix-core kernel's 4 waves take 8 tiles of 32 positions
     // per 256 (shorter splits cost more in epilogue and merge than they
     // gain), the VALU kernel's rows are shorter; and at most kMaxSplits
-    // splits per sequence (merged in groups of kSplitGroup).
+    // splits per sequence (beyond kMaxFusedSplits merged by a second kernel).
     const int min_chunk = kind == KIND_MFMA ? 256 : 32;
     if (chunk < min_chunk) chunk = min_chunk;
     const int min_for_merge = (int)round_up((size_t)ceil_div(Lmax, kMaxSplits), 32);
@@ -148,19 +144,17 @@ gqa_status make_plan(int B, int H, int G, int d, int Lmax, gqa_dtype dt, Plan *p
   const unsigned long long grid = (unsigned long long)units * pl->S;
   if (grid == 0 || grid > 0x7fffffffULL) return GQA_ERR_SIZE;
   pl->grid = (unsigned)grid;
-  pl->NG = pl->S > gqa::kOneLevel ? ceil_div(pl->S, gqa::kSplitGroup) : 0;
   const char *merge = getenv("GQA_MERGE");
-  // fused: one counter per unit, plus one per split group and unit
-  pl->fused = units * (1 + pl->NG) <= kMaxFusedUnits && !(merge && strcmp(merge, "kernel") == 0);
+  // In-kernel merge: one counter per unit, and a merging workgroup that
+  // reads every split of its heads, which pays up to kMaxFusedSplits; beyond
+  // that a merge kernel spread over heads, dimensions and splits.
+  pl->fused = units <= kMaxFusedUnits && pl->S <= kMaxFusedSplits && !(merge && strcmp(merge, "kernel") == 0);
   if (pl->S > 1) {
     pl->ml_off = kCounterBytes;
     pl->o_off = pl->ml_off + round_up((size_t)B * H * pl->S * sizeof(float2), 256);
-    pl->ml1_off = pl->o_off + round_up((size_t)B * H * pl->S * d * sizeof(float), 256);
-    pl->o1_off = pl->ml1_off + round_up((size_t)B * H * pl->NG * sizeof(float2), 256);
-    pl->ws_bytes = pl->NG ? pl->o1_off + (size_t)B * H * pl->NG * d * sizeof(float)
-                          : pl->o_off + (size_t)B * H * pl->S * d * sizeof(float);
+    pl->ws_bytes = pl->o_off + (size_t)B * H * pl->S * d * sizeof(float);
   } else {
-    pl->ml_off = pl->o_off = pl->ml1_off = pl->o1_off = pl->ws_bytes = 0;
+    pl->ml_off = pl->o_off = pl->ws_bytes = 0;
   }
   return GQA_OK;
 }
@@ -384,9 +378,6 @@ gqa_status decode_impl(int phase, const void *q, const void *k_new, const void *
   p.ws_cnt = pl.ws_bytes ? reinterpret_cast<unsigned *>(ws) : nullptr;
   p.ws_ml = pl.ws_bytes ? reinterpret_cast<float2 *>(ws + pl.ml_off) : nullptr;
   p.ws_o = pl.ws_bytes ? reinterpret_cast<float *>(ws + pl.o_off) : nullptr;
-  p.ws_ml1 = pl.NG ? reinterpret_cast<float2 *>(ws + pl.ml1_off) : nullptr;
-  p.ws_o1 = pl.NG ? reinterpret_cast<float *>(ws + pl.o1_off) : nullptr;
-  p.NG = pl.NG;
   p.fused = pl.fused;
   p.contig = env_int("GQA_CONTIG", 0) == 1;
   p.B = B;
@@ -406,8 +397,11 @@ gqa_status decode_impl(int phase, const void *q, const void *k_new, const void *
     if (e != hipSuccess) return hip_fail(e);
   }
   if (phase != 1 && pl.S > 1 && !pl.fused) {
-    // one merge workgroup per (sequence, K/V head): all r heads of the group
-    const hipError_t e = gqa::launch_merge(p, (int)dtype, d, p.r, stream);
+    // up to kMaxFusedSplits: one merge workgroup per (sequence, K/V head), all
+    // r heads of the group (the in-kernel merge's arithmetic); beyond, the
+    // wide merge kernel
+    const hipError_t e = pl.S <= kMaxFusedSplits ? gqa::launch_merge(p, (int)dtype, d, p.r, stream)
+                                                 : gqa::launch_merge_wide(p, (int)dtype, d, stream);
     if (e != hipSuccess) return hip_fail(e);
   }
   return GQA_OK;

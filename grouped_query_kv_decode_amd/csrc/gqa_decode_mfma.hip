@@ -392,7 +392,8 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma(DecodeParams p) {
     }
   }
   if (nsplit == 1 || !p.fused) return;
-  finish_splits<__bf16, D>(p, b, ((size_t)b * p.G + g) * p.HC + hc, head0, rw, s, nsplit);
+  if (!arrive_last(p.ws_cnt + ((size_t)b * p.G + g) * p.HC + hc, nsplit)) return;
+  merge_heads<__bf16, D>(p, b, head0, rw, nsplit);
 }
 
 template <int D, int HB, int NW>

@@ -240,7 +240,8 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeParams p) {
     }
   }
   if (nsplit == 1 || !p.fused) return;
-  finish_splits<T, D>(p, b, ((size_t)b * p.G + g) * p.HC + hc, head0, nh, s, nsplit);
+  if (!arrive_last(p.ws_cnt + ((size_t)b * p.G + g) * p.HC + hc, nsplit)) return;
+  merge_heads<T, D>(p, b, head0, nh, nsplit);
 }
 
 template <typename T, int D, int RC>

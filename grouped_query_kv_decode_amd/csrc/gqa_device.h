@@ -24,11 +24,7 @@ struct DecodeParams {
   void *out;               // [B, H, D]
   float *ws_o;             // [B, H, S, D]  un-normalised split outputs
   float2 *ws_ml;           // [B, H, S]     (running max in log2 units, sum of weights)
-  float *ws_o1;            // [B, H, NG, D] group partials (more than kOneLevel splits)
-  float2 *ws_ml1;          // [B, H, NG]
-  unsigned *ws_cnt;        // arrival counters; zero between calls: [0, units) per unit, then
-                           // NG per unit for the groups when NG > 0
-  int NG;                  // split groups per unit: 0 when S <= kOneLevel
+  unsigned *ws_cnt;        // arrival counter per unit; zero between calls
   int fused;               // 1: the last split of a unit merges; 0: a merge kernel follows
   int contig;              // matrix-core kernel: contiguous per-wave tile runs instead of interleaved tiles
   int B, H, G, Lmax;
@@ -155,119 +151,46 @@ __device__ __forceinline__ bool arrive_last(unsigned *counter, int nsplit) {
   return s_last != 0;
 }
 
-// Up to kOneLevel splits are merged in one fold by the last workgroup to
-// arrive.  Beyond that they are merged in groups of kSplitGroup: the last
-// arrival of each group folds the group into a group partial and the last
-// group to finish folds those, so no workgroup reads more than kSplitGroup
-// partials per head.  (At 32 splits one fold measured faster than two
-// levels; allowing 256 splits, merged in two levels, took one 131072-position
-// sequence of one K/V head from 70.7 to 22.3 us.)
-constexpr int kOneLevel = 32;
-constexpr int kSplitGroup = 16;
-
-// Running log-sum-exp state of one head's four output dimensions.
-struct Fold {
-  float M = kNegInf, L = 0.f, o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
-  // add a partial (max m, weight sum l, un-normalised output x, y)
-  __device__ __forceinline__ void add(float2 ml, float2 x, float2 y) {
-    const float mn = fmaxf(M, ml.x);
-    const float sh = safe_shift(mn);
-    const float a_old = fast_exp2(M - sh), a = fast_exp2(ml.x - sh);
-    M = mn;
-    L = L * a_old + ml.y * a;
-    o0 = o0 * a_old + x.x * a;
-    o1 = o1 * a_old + x.y * a;
-    o2 = o2 * a_old + y.x * a;
-    o3 = o3 * a_old + y.y * a;
-  }
-};
-
-// Fold partials first .. first+n-1 (in index order) of one head's list:
-// ml[i] and o[i * D + c .. +3].  Loads are issued sixteen at a time.
-template <int D>
-__device__ __forceinline__ void fold_range(Fold &f, const float2 *ml, const float *o, int c, int first, int n) {
-  constexpr int kBatch = 16;
-  for (int i0 = 0; i0 < n; i0 += kBatch) {
-    float2 h[kBatch], x[kBatch], y[kBatch];
-#pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
-      if (i0 + i < n) {
-        const int k = first + i0 + i;
-        h[i] = load_pair(reinterpret_cast<const float *>(ml + k));
-        x[i] = load_pair(o + (size_t)k * D + c);
-        y[i] = load_pair(o + (size_t)k * D + c + 2);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < kBatch; ++i)
-      if (i0 + i < n) f.add(h[i], x[i], y[i]);
-  }
-}
-
-template <typename T, int D>
-__device__ __forceinline__ void store_out(const DecodeParams &p, int b, int head, int c, const Fold &f) {
-  const float inv = 1.f / f.L;
-  Store<T>::four(p.out, ((size_t)b * p.H + head) * D + c, f.o0 * inv, f.o1 * inv, f.o2 * inv, f.o3 * inv);
-}
-
 // Log-sum-exp merge of the nsplit partials of heads head0 .. head0+nh-1 of
-// sequence b into out: one fold over the splits in index order, or, with
-// more than kOneLevel splits, a fold of each group followed by a fold of
-// the group results in group order - the arithmetic of the distributed
-// merge below, so both give the same bits.  Deterministic; the separate
-// merge kernel calls this same routine.
+// sequence b into out.  Splits are taken in index order, eight at a time: the
+// loads of a batch are issued together, then folded into a running
+// (max, weight sum, output) with rescaling when the max grows.  Deterministic;
+// the separate merge kernel calls this same routine.
 template <typename T, int D>
 __device__ void merge_heads(const DecodeParams &p, int b, int head0, int nh, int nsplit) {
+  constexpr int kBatch = 16;
   for (int idx = threadIdx.x; idx < nh * (D / 4); idx += blockDim.x) {
     const int j = idx / (D / 4), c = (idx % (D / 4)) * 4;
     const size_t hs = ((size_t)b * p.H + head0 + j) * p.S;
-    Fold f;
-    if (nsplit <= kOneLevel) {
-      fold_range<D>(f, p.ws_ml + hs, p.ws_o + hs * D, c, 0, nsplit);
-    } else {
-      for (int g0 = 0; g0 < nsplit; g0 += kSplitGroup) {
-        Fold fg;
-        fold_range<D>(fg, p.ws_ml + hs, p.ws_o + hs * D, c, g0, min(kSplitGroup, nsplit - g0));
-        f.add(make_float2(fg.M, fg.L), make_float2(fg.o0, fg.o1), make_float2(fg.o2, fg.o3));
+    const float *ml = reinterpret_cast<const float *>(p.ws_ml + hs);
+    float M = kNegInf, L = 0.f, o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+    for (int s0 = 0; s0 < nsplit; s0 += kBatch) {
+      float2 h[kBatch], x[kBatch], y[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        if (s0 + i < nsplit) {
+          h[i] = load_pair(ml + 2 * (s0 + i));
+          x[i] = load_pair(p.ws_o + (hs + s0 + i) * D + c);
+          y[i] = load_pair(p.ws_o + (hs + s0 + i) * D + c + 2);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        if (s0 + i < nsplit) {
+          const float mn = fmaxf(M, h[i].x);
+          const float sh = safe_shift(mn);
+          const float a_old = fast_exp2(M - sh), a = fast_exp2(h[i].x - sh);
+          M = mn;
+          L = L * a_old + h[i].y * a;
+          o0 = o0 * a_old + x[i].x * a;
+          o1 = o1 * a_old + x[i].y * a;
+          o2 = o2 * a_old + y[i].x * a;
+          o3 = o3 * a_old + y[i].y * a;
+        }
       }
     }
-    store_out<T, D>(p, b, head0 + j, c, f);
-  }
-}
-
-// After a workgroup has stored its split partial: the arrival protocol of
-// the in-kernel merge.  Every workgroup of a unit calls this; the last one
-// to arrive merges (two levels with more than kOneLevel splits: the last
-// of each group folds the group into a group partial, the last group folds
-// those).  unit = (b * G + g) * HC + hc.
-template <typename T, int D>
-__device__ void finish_splits(const DecodeParams &p, int b, size_t unit, int head0, int nh, int s, int nsplit) {
-  if (nsplit <= kOneLevel) {
-    if (!arrive_last(p.ws_cnt + unit, nsplit)) return;
-    merge_heads<T, D>(p, b, head0, nh, nsplit);
-    return;
-  }
-  const int gi = s / kSplitGroup;
-  const int g0 = gi * kSplitGroup;
-  const size_t units = (size_t)p.B * p.G * p.HC;
-  if (!arrive_last(p.ws_cnt + units + unit * p.NG + gi, min(kSplitGroup, nsplit - g0))) return;
-  for (int idx = threadIdx.x; idx < nh * (D / 4); idx += blockDim.x) {
-    const int j = idx / (D / 4), c = (idx % (D / 4)) * 4;
-    const size_t hs = ((size_t)b * p.H + head0 + j) * p.S;
-    Fold fg;
-    fold_range<D>(fg, p.ws_ml + hs, p.ws_o + hs * D, c, g0, min(kSplitGroup, nsplit - g0));
-    const size_t hg = ((size_t)b * p.H + head0 + j) * p.NG + gi;
-    store_partial4(p.ws_o1 + hg * D + c, fg.o0, fg.o1, fg.o2, fg.o3);
-    if (c == 0) store_ml(p.ws_ml1 + hg, fg.M, fg.L);
-  }
-  const int ng = (nsplit + kSplitGroup - 1) / kSplitGroup;
-  if (!arrive_last(p.ws_cnt + unit, ng)) return;
-  for (int idx = threadIdx.x; idx < nh * (D / 4); idx += blockDim.x) {
-    const int j = idx / (D / 4), c = (idx % (D / 4)) * 4;
-    const size_t hg = ((size_t)b * p.H + head0 + j) * p.NG;
-    Fold f;
-    fold_range<D>(f, p.ws_ml1 + hg, p.ws_o1 + hg * D, c, 0, ng);
-    store_out<T, D>(p, b, head0 + j, c, f);
+    const float inv = 1.f / L;
+    Store<T>::four(p.out, ((size_t)b * p.H + head0 + j) * D + c, o0 * inv, o1 * inv, o2 * inv, o3 * inv);
   }
 }
 
@@ -275,6 +198,7 @@ __device__ void finish_splits(const DecodeParams &p, int b, size_t unit, int hea
 hipError_t launch_decode_valu(const DecodeParams &p, int dtype, int D, int RC, unsigned grid, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeParams &p, int D, int HB, int NW, unsigned grid, hipStream_t stream);
 hipError_t launch_merge(const DecodeParams &p, int dtype, int D, int heads_per_unit, hipStream_t stream);
+hipError_t launch_merge_wide(const DecodeParams &p, int dtype, int D, hipStream_t stream);
 hipError_t launch_meanpool(const float *w, int d_model, int H, int G, int h, float *w_out, hipStream_t stream);
 hipError_t launch_fill_zero(void *ptr, size_t bytes, hipStream_t stream);
 

@@ -1,6 +1,6 @@
-// Log-sum-exp merge of context-split partials into the decode output, as a
-// separate kernel (used when the in-kernel merge is off), and the workspace
-// fill kernel.
+// Log-sum-exp merge of context-split partials into the decode output, as
+// separate kernels (used when the in-kernel merge is off, and beyond 32
+// splits per sequence), and the workspace fill kernel.
 //
 // A split s of head h leaves (m_s, l_s, o_s): the maximum of its scores in
 // log2 units, the sum of exp2(score - m_s) over its positions, and the
@@ -27,6 +27,77 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p, int heads_pe
   merge_heads<T, D>(p, b, head0, heads_per_unit, nsplit);
 }
 
+// Many splits (up to 256 per sequence, for few and long sequences): one
+// workgroup per (sequence, head, 32 output dimensions), 256 threads = 8 groups
+// of 4 dimensions x 32 slices of consecutive splits.  Each thread folds its
+// slice; the slices are then folded in slice order through LDS, so the result
+// is deterministic, and no thread reads more than ceil(nsplit / 32) partials
+// (one batch of loads at 256 splits).
+struct Fold {
+  float M = kNegInf, L = 0.f, o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+  __device__ __forceinline__ void add(float m, float l, float x0, float x1, float x2, float x3) {
+    const float mn = fmaxf(M, m);
+    const float sh = safe_shift(mn);
+    const float a_old = fast_exp2(M - sh), a = fast_exp2(m - sh);
+    M = mn;
+    L = L * a_old + l * a;
+    o0 = o0 * a_old + x0 * a;
+    o1 = o1 * a_old + x1 * a;
+    o2 = o2 * a_old + x2 * a;
+    o3 = o3 * a_old + x3 * a;
+  }
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void merge_wide_kernel(DecodeParams p) {
+  constexpr int kSlices = 32, kBatch = 16;
+  const int bh = blockIdx.x / (D / 32);  // b * H + head
+  const int b = bh / p.H;
+  const int n = clamp_len(p, b);
+  const int nsplit = num_splits(n - window_lo(p, n), p.chunk);
+  if (nsplit <= 1) return;  // written directly by the split kernel
+  const int q = threadIdx.x & 7, k = threadIdx.x >> 3;
+  const int c = (blockIdx.x % (D / 32)) * 32 + 4 * q;
+  const int per = (nsplit + kSlices - 1) / kSlices;
+  const int first = k * per;
+  const int cnt = min(per, nsplit - first);
+  const float *ml = reinterpret_cast<const float *>(p.ws_ml + (size_t)bh * p.S);
+  const float *o = p.ws_o + (size_t)bh * p.S * D + c;
+  Fold f;
+  for (int i0 = 0; i0 < cnt; i0 += kBatch) {
+    float2 h[kBatch], x[kBatch], y[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      if (i0 + i < cnt) {
+        const int s = first + i0 + i;
+        h[i] = load_pair(ml + 2 * s);
+        x[i] = load_pair(o + (size_t)s * D);
+        y[i] = load_pair(o + (size_t)s * D + 2);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i)
+      if (i0 + i < cnt) f.add(h[i].x, h[i].y, x[i].x, x[i].y, y[i].x, y[i].y);
+  }
+  __shared__ float sm[kSlices][8][6];
+  float *e = sm[k][q];
+  e[0] = f.M;
+  e[1] = f.L;
+  e[2] = f.o0;
+  e[3] = f.o1;
+  e[4] = f.o2;
+  e[5] = f.o3;
+  __syncthreads();
+  if (k != 0) return;
+  Fold t;
+  for (int kk = 0; kk < kSlices && kk * per < nsplit; ++kk) {
+    const float *v = sm[kk][q];
+    t.add(v[0], v[1], v[2], v[3], v[4], v[5]);
+  }
+  const float inv = 1.f / t.L;
+  Store<T>::four(p.out, (size_t)bh * D + c, t.o0 * inv, t.o1 * inv, t.o2 * inv, t.o3 * inv);
+}
+
 template <typename T>
 hipError_t launch_t(const DecodeParams &p, int D, int heads_per_unit, hipStream_t stream) {
   const unsigned grid = (unsigned)((size_t)p.B * (p.H / heads_per_unit));
@@ -47,6 +118,22 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(uint4 *p, size_t n16, un
 
 hipError_t launch_merge(const DecodeParams &p, int dtype, int D, int heads_per_unit, hipStream_t stream) {
   return dtype == 0 ? launch_t<float>(p, D, heads_per_unit, stream) : launch_t<__bf16>(p, D, heads_per_unit, stream);
+}
+
+hipError_t launch_merge_wide(const DecodeParams &p, int dtype, int D, hipStream_t stream) {
+  const unsigned grid = (unsigned)((size_t)p.B * p.H * (D / 32));
+  if (dtype == 0) {
+    if (D == 64)
+      hipLaunchKernelGGL((merge_wide_kernel<float, 64>), dim3(grid), dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL((merge_wide_kernel<float, 128>), dim3(grid), dim3(256), 0, stream, p);
+  } else {
+    if (D == 64)
+      hipLaunchKernelGGL((merge_wide_kernel<__bf16, 64>), dim3(grid), dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL((merge_wide_kernel<__bf16, 128>), dim3(grid), dim3(256), 0, stream, p);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_fill_zero(void *ptr, size_t bytes, hipStream_t stream) {

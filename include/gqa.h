@@ -103,10 +103,10 @@ gqa_status gqa_workspace_init(void *workspace, size_t workspace_bytes, hipStream
  * few (sequence, K/V head) units, the group's heads are spread over 2 or 4
  * workgroups that read the same part); when a sequence spans several splits
  * (at most 256), the workgroup that finishes its unit last merges the split
- * results (log-sum-exp) into out - in two levels beyond 32 splits: the last
- * of each group of 16 merges the group, the last group merges the groups.
- * When the counters of that protocol exceed 65536, or with the environment
- * variable GQA_MERGE=kernel, a second kernel does the merge instead.  The
+ * results (log-sum-exp) into out.  Beyond 32 splits per sequence, above 65536
+ * units, or with the environment variable GQA_MERGE=kernel, a second kernel
+ * does that merge instead (beyond 32 splits one spread over sequences, heads,
+ * dimensions and slices of the splits).  The
  * call allocates nothing, does not synchronise and issues no memset, so it
  * can be captured into a HIP graph (with a workspace cleared beforehand).
  * NaN or Inf inside the attended positions propagate to the output.

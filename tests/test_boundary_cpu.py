@@ -107,14 +107,7 @@ def test_workspace_size_model(lib, monkeypatch):
 
 
 def _decode_ws(B, H, S, d):
-    """Counters, split (max, sum) and outputs; with more than 32 splits also
-    the results of the split groups (16 splits each)."""
-    up = lambda x: (x + 255) // 256 * 256
-    ws = 256 * 1024 + up(B * H * S * 8) + B * H * S * d * 4
-    if S > 32:
-        ng = (S + 15) // 16
-        ws = 256 * 1024 + up(B * H * S * 8) + up(B * H * S * d * 4) + up(B * H * ng * 8) + B * H * ng * d * 4
-    return ws
+    return 256 * 1024 + (B * H * S * 8 + 255) // 256 * 256 + B * H * S * d * 4
 
 
 def test_split_plan_model(lib, monkeypatch):

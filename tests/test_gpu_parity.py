@@ -110,13 +110,13 @@ def test_small_parity(env, case, dtype, kernel, chunk, merge):
     check(out, oracle_out(q, k, v, lens_t, scale), dtype, "%s %s chunk=%s %s" % (dtype, kernel, chunk, case))
 
 
-# Many splits per sequence: beyond 32 the in-kernel merge has two levels
-# (the last of each group of 16 splits folds the group, the last group folds
-# the groups).  Units with one group, several groups and a partial last group
-# side by side.
+# Many splits per sequence: beyond 32 the splits are merged by the wide merge
+# kernel (a workgroup per sequence, head and 32 dimensions; 32 slices of
+# splits folded in order).  Sequences with few and with many splits side by
+# side; slice counts that do not divide the splits.
 MANY_SPLITS = [
     # (B, H, G, d, Lmax, lens, chunk)
-    (3, 32, 8, 128, 9000, [9000, 4100, 300], 256),     # 36 splits (16 + 16 + 4), 17, 2
+    (3, 32, 8, 128, 9000, [9000, 4100, 300], 256),     # 36 splits, 17, 2
     (2, 8, 1, 128, 20000, [20000, 16 * 256 + 1], 256),  # r = 8: 79 splits; 17
     (2, 64, 1, 64, 12000, [12000, 5000], 256),         # head chunks: 47 and 20 splits
     (1, 8, 2, 64, 8192, [8192], 32),                    # 256 splits, the planner's maximum
@@ -159,7 +159,7 @@ def test_many_splits_window_and_append(env):
 
 def test_long_single_sequence(env):
     """One sequence, one K/V head, 131072 positions: the planner's 256 splits
-    of 512 positions (every compute unit busy), two-level merge."""
+    of 512 positions (every compute unit busy), merged by the wide kernel."""
     w = wl.Workload("long", 1, 8, 1, 128, 131072, "bf16", 41)
     q, k, v, lens = wl.make_inputs(w, DEV)
     out = run_gpu(q, k, v, lens, w.scale)
@@ -329,7 +329,7 @@ def test_fused_merge_matches_merge_kernel(env, kernel):
     cases = [rand_case(16, 32, 8, 128, 4096, [4096] * 16, "bf16", seed=21),
              rand_case(32, 64, 8, 64, 2048, [2048 - 37 * i for i in range(32)], "bf16", seed=22),
              rand_case(4, 16, 4, 128, 3000, [3000, 1, 1500, 2999], "f32", seed=23),
-             rand_case(3, 32, 8, 128, 9000, [9000, 4100, 300], "bf16", seed=24)]  # 36 splits: two levels
+             rand_case(3, 32, 8, 128, 9000, [9000, 4100, 300], "bf16", seed=24)]  # 36 splits: wide merge
     for q, k, v, lens, scale in cases:
         env(GQA_KERNEL=None if kernel == "default" else kernel, GQA_CHUNK=256, GQA_MERGE="kernel")
         ref = run_gpu(q, k, v, lens, scale).clone()
