@@ -40,7 +40,7 @@ def env(monkeypatch):
             else:
                 monkeypatch.setenv(k, str(v))
     set_(GQA_KERNEL=None, GQA_CHUNK=None, GQA_TARGET_WGS=None, GQA_MAX_CHUNK=None, GQA_MERGE=None, GQA_WAVES=None,
-         GQA_CONTIG=None, GQA_HEAD_SPLIT=None)
+         GQA_CONTIG=None, GQA_HEAD_SPLIT=None, GQA_FUSED_MAX_SPLITS=None)
     return set_
 
 
@@ -100,11 +100,13 @@ SMALL = [
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("kernel", ["default", "valu"])
 @pytest.mark.parametrize("chunk", [None, 32, 128, 100000])
-@pytest.mark.parametrize("merge", ["fused", "kernel"])
+@pytest.mark.parametrize("merge", ["fused", "kernel", "wide"])
 def test_small_parity(env, case, dtype, kernel, chunk, merge):
+    """merge: in the decode kernel, the per-unit merge kernel, or the wide
+    merge kernel (forced for every split plan)."""
     B, H, G, d, L, lens = case
     env(GQA_KERNEL=None if kernel == "default" else kernel, GQA_CHUNK=chunk,
-        GQA_MERGE=None if merge == "fused" else "kernel")
+        GQA_MERGE="kernel" if merge == "kernel" else None, GQA_FUSED_MAX_SPLITS=1 if merge == "wide" else None)
     q, k, v, lens_t, scale = rand_case(B, H, G, d, L, lens, dtype, seed=sum(case[:5]) + 7 * len(lens))
     out = run_gpu(q, k, v, lens_t, scale)
     check(out, oracle_out(q, k, v, lens_t, scale), dtype, "%s %s chunk=%s %s" % (dtype, kernel, chunk, case))
