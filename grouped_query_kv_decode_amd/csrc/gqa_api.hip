@@ -73,7 +73,9 @@ gqa_status check_shape(int B, int H, int G, int d, int Lmax, gqa_dtype dt) {
 //  - workgroups of the matrix-core kernel have 4 waves (GQA_WAVES = 8 or 16
 //    overrides where the register budget for the head blocks allows).
 //  - with fewer (b, g) units than compute units the matrix-core kernel
-//    spreads a group's head blocks over 2 or 4 workgroups (GQA_HEAD_SPLIT).
+//    spreads a group's head blocks over 2 or 4 workgroups (GQA_HEAD_SPLIT),
+//    which then load the cache with plain instead of non-temporal loads
+//    (GQA_TEMPORAL=0/1 overrides) so that they share its lines in L2.
 //  - splits: one workgroup per (b, g, head chunk, split).  The split length
 //    is chosen so that the grid holds about GQA_TARGET_WGS = 256 workgroups
 //    (one per compute unit), at least 256 positions (matrix cores) or 32

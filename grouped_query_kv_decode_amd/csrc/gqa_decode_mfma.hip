@@ -75,7 +75,7 @@ __device__ __forceinline__ void pv_steps(f32x4 (&o)[HB][DB], const Row *vR, cons
   }
 }
 
-template <int D, int HB, int NW, int TPI>
+template <int D, int HB, int NW, int TPI, bool NT>
 __global__ __launch_bounds__(64 * NW) void decode_mfma(DecodeParams p) {
   static_assert(D == 64 || D == 128, "head dim");
   static_assert(TPI == 1 || TPI == 2, "tiles per iteration");
@@ -126,6 +126,15 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma(DecodeParams p) {
   const int koff = (8 * (nn >> 2) + (nn & 3)) * D + 8 * c;
   const int voff = 8 * c * D + VPL * nn;
 
+  // Cache loads: non-temporal, or plain where the head chunks of a group read
+  // the same tiles (they then find each other's lines in L2).
+  auto kv_load = [](const auto *ptr) {
+    if constexpr (NT)
+      return stream_load(ptr);
+    else
+      return *ptr;
+  };
+
   // One 32-position tile: K rows for the two score halves, V rows 8c .. 8c+7.
   struct Tile {
     u32x4 kA[2][KB];
@@ -142,9 +151,9 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma(DecodeParams p) {
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
-        T.kA[h][kb] = stream_load(reinterpret_cast<const u32x4 *>(kt + koff + h * 4 * D + kb * 32));
+        T.kA[h][kb] = kv_load(reinterpret_cast<const u32x4 *>(kt + koff + h * 4 * D + kb * 32));
 #pragma unroll
-    for (int u = 0; u < 8; ++u) T.vR[u] = stream_load(reinterpret_cast<const VRow *>(vt + voff + u * D));
+    for (int u = 0; u < 8; ++u) T.vR[u] = kv_load(reinterpret_cast<const VRow *>(vt + voff + u * D));
   };
 
   // The wave's first tile is requested before the sequence length arrives
@@ -197,13 +206,13 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma(DecodeParams p) {
       const int t = min(tt + 8 * (nn >> 2) + 4 * h + (nn & 3), t1 - 1);
       const __bf16 *src = (append && t == n - 1) ? knew : kbase + (size_t)t * D;
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) T.kA[h][kb] = stream_load(reinterpret_cast<const u32x4 *>(src + 8 * c + kb * 32));
+      for (int kb = 0; kb < KB; ++kb) T.kA[h][kb] = kv_load(reinterpret_cast<const u32x4 *>(src + 8 * c + kb * 32));
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int t = min(tt + 8 * c + u, t1 - 1);
       const __bf16 *src = (append && t == n - 1) ? vnew : vbase + (size_t)t * D;
-      T.vR[u] = stream_load(reinterpret_cast<const VRow *>(src + VPL * nn));
+      T.vR[u] = kv_load(reinterpret_cast<const VRow *>(src + VPL * nn));
     }
   };
   // Scores, softmax weights and the weighted V sum of one tile.  The running
@@ -400,7 +409,15 @@ template <int D, int HB, int NW>
 hipError_t launch_t(const DecodeParams &p, unsigned grid, hipStream_t stream) {
   // d = 64 tiles are half as long: two per iteration keep as many bytes in flight
   constexpr int TPI = D == 64 ? 2 : 1;
-  hipLaunchKernelGGL((decode_mfma<D, HB, NW, TPI>), dim3(grid), dim3(64 * NW), 0, stream, p);
+  const char *env = getenv("GQA_TEMPORAL");
+  const bool temporal = env && env[0] ? env[0] == '1' : p.HC > 1;
+  if constexpr (HB <= 2) {
+    if (temporal) {
+      hipLaunchKernelGGL((decode_mfma<D, HB, NW, TPI, false>), dim3(grid), dim3(64 * NW), 0, stream, p);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((decode_mfma<D, HB, NW, TPI, true>), dim3(grid), dim3(64 * NW), 0, stream, p);
   return hipGetLastError();
 }
 
