@@ -42,21 +42,24 @@ enum { KIND_VALU = 0, KIND_MFMA = 1 };
 //                       zero between calls (each call leaves them zero)
 //   ml region           float2 [B, H, S]   split (max, weight sum)
 //   o region            float  [B, H, S, d] split un-normalised outputs
+//   order region        int    [grid]       dispatch order (multi-round grids)
 // The counter region is never used for anything else, whatever the shape,
 // so one cleared workspace serves calls of any shape.
 constexpr size_t kCounterBytes = 256 * 1024;
 constexpr long kMaxFusedUnits = kCounterBytes / sizeof(unsigned);  // counters
 constexpr int kMaxSplits = 256;     // splits per sequence the planner uses at most
 constexpr int kMaxFusedSplits = 32; // more splits: merged by the wide merge kernel
+constexpr unsigned kOrderMinGrid = 1024;  // larger split grids run largest items first
 
 struct Plan {
   int kind;
   int chunk, S, HC, RC, HB;
   int NW;  // waves per workgroup (matrix-core kernel)
   int fused;
-  int wide;  // merge by the wide merge kernel
+  int wide;     // merge by the wide merge kernel
+  int ordered;  // workgroups take their items largest first (order region of the workspace)
   unsigned grid;
-  size_t ml_off, o_off, ws_bytes;
+  size_t ml_off, o_off, order_off, ws_bytes;
 };
 
 gqa_status check_shape(int B, int H, int G, int d, int Lmax, gqa_dtype dt) {
@@ -157,12 +160,19 @@ gqa_status make_plan(int B, int H, int G, int d, int Lmax, gqa_dtype dt, Plan *p
   // that a merge kernel spread over heads, dimensions and splits.
   pl->wide = pl->S > env_int("GQA_FUSED_MAX_SPLITS", kMaxFusedSplits);
   pl->fused = units <= kMaxFusedUnits && !pl->wide && !(merge && strcmp(merge, "kernel") == 0);
+  // Grids of several rounds with several splits per sequence: the order
+  // kernel sorts the items largest first (ragged lengths otherwise leave
+  // whole splits of the longest sequences to the last round).
+  const char *ord = getenv("GQA_ORDER");
+  pl->ordered = pl->S > 1 && pl->grid > kOrderMinGrid && !(ord && strcmp(ord, "0") == 0);
   if (pl->S > 1) {
     pl->ml_off = kCounterBytes;
     pl->o_off = pl->ml_off + round_up((size_t)B * H * pl->S * sizeof(float2), 256);
-    pl->ws_bytes = pl->o_off + (size_t)B * H * pl->S * d * sizeof(float);
+    pl->order_off = pl->o_off + round_up((size_t)B * H * pl->S * d * sizeof(float), 256);
+    pl->ws_bytes = pl->ordered ? pl->order_off + (size_t)pl->grid * sizeof(int)
+                               : pl->o_off + (size_t)B * H * pl->S * d * sizeof(float);
   } else {
-    pl->ml_off = pl->o_off = pl->ws_bytes = 0;
+    pl->ml_off = pl->o_off = pl->order_off = pl->ws_bytes = 0;
   }
   return GQA_OK;
 }
@@ -386,6 +396,8 @@ gqa_status decode_impl(int phase, const void *q, const void *k_new, const void *
   p.ws_cnt = pl.ws_bytes ? reinterpret_cast<unsigned *>(ws) : nullptr;
   p.ws_ml = pl.ws_bytes ? reinterpret_cast<float2 *>(ws + pl.ml_off) : nullptr;
   p.ws_o = pl.ws_bytes ? reinterpret_cast<float *>(ws + pl.o_off) : nullptr;
+  int *order = pl.ordered ? reinterpret_cast<int *>(ws + pl.order_off) : nullptr;
+  p.order = order;
   p.fused = pl.fused;
   p.contig = env_int("GQA_CONTIG", 0) == 1;
   p.B = B;
@@ -399,6 +411,10 @@ gqa_status decode_impl(int phase, const void *q, const void *k_new, const void *
   p.HC = pl.HC;
   p.scale_log2 = (float)sl2;
 
+  if (phase != 2 && order) {
+    const hipError_t e = gqa::launch_order(p, pl.kind == KIND_VALU, pl.grid, order, stream);
+    if (e != hipSuccess) return hip_fail(e);
+  }
   if (phase != 2) {
     const hipError_t e = pl.kind == KIND_MFMA ? gqa::launch_decode_mfma(p, d, pl.HB, pl.NW, pl.grid, stream)
                                               : gqa::launch_decode_valu(p, (int)dtype, d, pl.RC, pl.grid, stream);

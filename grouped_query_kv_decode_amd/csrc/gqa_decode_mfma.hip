@@ -93,10 +93,13 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma(DecodeParams p) {
   // chunks of one (b, g, split) are B*G apart in dispatch order - on the same
   // XCD when B*G is a multiple of 8, so the tiles they all read come from
   // that XCD's L2 after the first.
+  // (With p.order, the workgroups take the items in the order it gives:
+  // largest work first, for grids that run in several rounds.)
+  const unsigned item = p.order ? (unsigned)p.order[blockIdx.x] : blockIdx.x;
   const unsigned bg = (unsigned)p.B * p.G;
   const unsigned units = bg * p.HC;
-  const int s = blockIdx.x / units;
-  const unsigned rem = blockIdx.x % units;
+  const int s = item / units;
+  const unsigned rem = item % units;
   const int hc = rem / bg;
   const unsigned u = rem % bg;
   const int g = u % p.G;

@@ -64,9 +64,10 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeParams p) {
   const int rg = wave * RPW + lane / LPR;
 
   // Split index slowest (see the MFMA kernel): units spread over the XCDs.
+  const unsigned item = p.order ? (unsigned)p.order[blockIdx.x] : blockIdx.x;
   const unsigned units = (unsigned)p.B * p.G * p.HC;
-  const int s = blockIdx.x / units;
-  unsigned id = blockIdx.x % units;
+  const int s = item / units;
+  unsigned id = item % units;
   const int hc = id % p.HC;
   id /= p.HC;
   const int g = id % p.G;

@@ -25,6 +25,7 @@ struct DecodeParams {
   float *ws_o;             // [B, H, S, D]  un-normalised split outputs
   float2 *ws_ml;           // [B, H, S]     (running max in log2 units, sum of weights)
   unsigned *ws_cnt;        // arrival counter per unit; zero between calls
+  const int *order;        // item of each workgroup (largest work first), or null: item = blockIdx
   int fused;               // 1: the last split of a unit merges; 0: a merge kernel follows
   int contig;              // matrix-core kernel: contiguous per-wave tile runs instead of interleaved tiles
   int B, H, G, Lmax;
@@ -199,6 +200,7 @@ hipError_t launch_decode_valu(const DecodeParams &p, int dtype, int D, int RC, u
 hipError_t launch_decode_mfma(const DecodeParams &p, int D, int HB, int NW, unsigned grid, hipStream_t stream);
 hipError_t launch_merge(const DecodeParams &p, int dtype, int D, int heads_per_unit, hipStream_t stream);
 hipError_t launch_merge_wide(const DecodeParams &p, int dtype, int D, hipStream_t stream);
+hipError_t launch_order(const DecodeParams &p, bool valu_layout, unsigned grid, int *order, hipStream_t stream);
 hipError_t launch_meanpool(const float *w, int d_model, int H, int G, int h, float *w_out, hipStream_t stream);
 hipError_t launch_fill_zero(void *ptr, size_t bytes, hipStream_t stream);
 

@@ -106,14 +106,20 @@ def test_workspace_size_model(lib, monkeypatch):
     assert lib.gqa_decode_workspace_size(B, 6, 4, d, L, BF16) == 0  # rejected shape
 
 
-def _decode_ws(B, H, S, d):
-    return 256 * 1024 + (B * H * S * 8 + 255) // 256 * 256 + B * H * S * d * 4
+def _decode_ws(B, H, S, d, grid=0):
+    """Counters, split (max, sum) pairs, split outputs; for grids of more than
+    1024 workgroups (with splits) also the dispatch order, one int each."""
+    up = lambda x: (x + 255) // 256 * 256
+    if grid > 1024:
+        return 256 * 1024 + up(B * H * S * 8) + up(B * H * S * d * 4) + grid * 4
+    return 256 * 1024 + up(B * H * S * 8) + B * H * S * d * 4
 
 
 def test_split_plan_model(lib, monkeypatch):
     """Split lengths: about 256 workgroups, at least 256 positions on the
     matrix cores (32 on the VALU kernel), at least Lmax/256, at most 4096."""
-    for k in ("GQA_CHUNK", "GQA_TARGET_WGS", "GQA_MAX_CHUNK", "GQA_KERNEL", "GQA_HEAD_SPLIT", "GQA_MERGE"):
+    for k in ("GQA_CHUNK", "GQA_TARGET_WGS", "GQA_MAX_CHUNK", "GQA_KERNEL", "GQA_HEAD_SPLIT", "GQA_MERGE", "GQA_ORDER",
+              "GQA_FUSED_MAX_SPLITS"):
         monkeypatch.delenv(k, raising=False)
     cases = [
         # (B, H, G, d, L, dtype, splits)
@@ -121,15 +127,17 @@ def test_split_plan_model(lib, monkeypatch):
         (1, 32, 8, 128, 4096, BF16, 16),      # 8 units: 256-position floor
         (4, 32, 8, 128, 4096, BF16, 8),       # 32 units: 512
         (1, 32, 8, 128, 32768, BF16, 32),     # 8 units, long: 1024 (256 WGs)
-        (64, 64, 8, 128, 32768, BF16, 8),     # 512 units: 4096 cap
+        (64, 64, 8, 128, 32768, BF16, 8, 4096),  # 512 units: 4096 cap; 4096 workgroups, ordered
         (8, 32, 16, 128, 8192, BF16, 2),      # 128 units: 4096
         (1, 8, 2, 64, 256, F32, 8),           # VALU, 2 units: 32-position floor
         (1, 8, 2, 64, 8192, F32, 128),        # VALU, 2 units: 64-position splits
         (1, 8, 1, 128, 131072, BF16, 256),    # one unit, long: 512-position splits (256 WGs)
         (1, 8, 1, 128, 262144, F32, 256),     # at most 256 splits: 1024 positions
     ]
-    for B, H, G, d, L, dt, S in cases:
-        assert lib.gqa_decode_workspace_size(B, H, G, d, L, dt) == _decode_ws(B, H, S, d), (B, H, G, d, L, dt, S)
+    for B, H, G, d, L, dt, S, *grid in cases:
+        assert lib.gqa_decode_workspace_size(B, H, G, d, L, dt) == _decode_ws(B, H, S, d, *grid), (B, H, G, d, L, dt, S)
+    monkeypatch.setenv("GQA_ORDER", "0")  # no dispatch order: no order region
+    assert lib.gqa_decode_workspace_size(64, 64, 8, 128, 32768, BF16) == _decode_ws(64, 64, 8, 128)
     # one split: no workspace
     assert lib.gqa_decode_workspace_size(32, 64, 8, 64, 2048, BF16) == 0
 

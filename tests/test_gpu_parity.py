@@ -40,7 +40,7 @@ def env(monkeypatch):
             else:
                 monkeypatch.setenv(k, str(v))
     set_(GQA_KERNEL=None, GQA_CHUNK=None, GQA_TARGET_WGS=None, GQA_MAX_CHUNK=None, GQA_MERGE=None, GQA_WAVES=None,
-         GQA_CONTIG=None, GQA_HEAD_SPLIT=None, GQA_FUSED_MAX_SPLITS=None)
+         GQA_CONTIG=None, GQA_HEAD_SPLIT=None, GQA_FUSED_MAX_SPLITS=None, GQA_ORDER=None)
     return set_
 
 
@@ -166,6 +166,44 @@ def test_long_single_sequence(env):
     q, k, v, lens = wl.make_inputs(w, DEV)
     out = run_gpu(q, k, v, lens, w.scale)
     check(out, oracle_out(q, k, v, lens, w.scale), "bf16", "B1 H8 G1 d128 L131072")
+
+
+@pytest.mark.parametrize("dtype,kernel", [("bf16", "default"), ("f32", "default"), ("bf16", "valu")])
+def test_dispatch_order(env, dtype, kernel):
+    """Grids of more than 1024 workgroups with several splits run their items
+    largest first (an order kernel sorts them on the device): only the
+    schedule changes, so outputs are bit-equal to blockIdx order - with the
+    in-kernel merge, the merge kernel, a window and a cache append - and
+    agree with the oracle."""
+    B, H, G, d, L = 48, 32, 8, 128, 6000
+    gen = torch.Generator().manual_seed(71)
+    lens = [int(x) for x in torch.randint(1, L + 1, (B,), generator=gen)]
+    lens[:3] = [L, 1, 513]
+    q, k, v, lt, scale = rand_case(B, H, G, d, L, lens, dtype, seed=72)
+    kernel_env = None if kernel == "default" else kernel
+    for merge in (None, "kernel"):
+        env(GQA_KERNEL=kernel_env, GQA_CHUNK=256, GQA_MERGE=merge, GQA_ORDER=0)   # 384 units x 24 splits
+        ref = run_gpu(q, k, v, lt, scale).clone()
+        env(GQA_ORDER=None)
+        for _ in range(3):
+            assert torch.equal(run_gpu(q, k, v, lt, scale), ref)
+    check(ref[:8], oracle_out(q, k, v, lt, scale, rows=list(range(8))), dtype, "ordered grid, sampled rows")
+    env(GQA_ORDER=0)
+    ref_w = gqa.decode_window(q, k, v, lt, scale, window=2500).clone()
+    env(GQA_ORDER=None)
+    assert torch.equal(gqa.decode_window(q, k, v, lt, scale, window=2500), ref_w)
+    gen = torch.Generator(DEV).manual_seed(73)
+    dt = torch.float32 if dtype == "f32" else torch.bfloat16
+    kn = torch.randn((B, G, d), generator=gen, device=DEV).to(dt)
+    vn = torch.randn((B, G, d), generator=gen, device=DEV).to(dt)
+    k0, v0 = k.clone(), v.clone()
+    env(GQA_ORDER=0)
+    ref_a = gqa.decode_append(q, kn, vn, k0, v0, lt, scale).clone()
+    env(GQA_ORDER=None)
+    k1, v1 = k.clone(), v.clone()
+    assert torch.equal(gqa.decode_append(q, kn, vn, k1, v1, lt, scale), ref_a)
+    bits = torch.int32 if dtype == "f32" else torch.int16
+    assert torch.equal(k1.view(bits), k0.view(bits)) and torch.equal(v1.view(bits), v0.view(bits))
 
 
 def test_tiny_workload_fp32(env):
