@@ -49,7 +49,8 @@ constexpr size_t kCounterBytes = 256 * 1024;
 constexpr long kMaxFusedUnits = kCounterBytes / sizeof(unsigned);  // counters
 constexpr int kMaxSplits = 256;     // splits per sequence the planner uses at most
 constexpr int kMaxFusedSplits = 32; // more splits: merged by the wide merge kernel
-constexpr unsigned kOrderMinGrid = 1024;  // larger split grids run largest items first
+constexpr unsigned kOrderMinGrid = 1024;  // larger split grids run largest items first ...
+constexpr int kOrderMinSplits = 4;        // ... with at least this many splits per sequence
 
 struct Plan {
   int kind;
@@ -160,11 +161,16 @@ gqa_status make_plan(int B, int H, int G, int d, int Lmax, gqa_dtype dt, Plan *p
   // that a merge kernel spread over heads, dimensions and splits.
   pl->wide = pl->S > env_int("GQA_FUSED_MAX_SPLITS", kMaxFusedSplits);
   pl->fused = units <= kMaxFusedUnits && !pl->wide && !(merge && strcmp(merge, "kernel") == 0);
-  // Grids of several rounds with several splits per sequence: the order
-  // kernel sorts the items largest first (ragged lengths otherwise leave
-  // whole splits of the longest sequences to the last round).
+  // Grids of several rounds with at least kOrderMinSplits splits per
+  // sequence: the order kernel sorts the items largest first (ragged lengths
+  // otherwise leave whole splits of the longest sequences to the last round:
+  // ragged B64 H64 G8 d128 Lmax 32768, 8 splits, 785 -> 725 us).  It costs
+  // each workgroup one dependent load at its start, ~1% on a batch of equal
+  // lengths (B64 H32 G16 d128 L8192, 2 splits: 646.7 -> 654.6 us), hence the
+  // split floor.
   const char *ord = getenv("GQA_ORDER");
-  pl->ordered = pl->S > 1 && pl->grid > kOrderMinGrid && !(ord && strcmp(ord, "0") == 0);
+  pl->ordered = (pl->S >= kOrderMinSplits && pl->grid > kOrderMinGrid && !(ord && strcmp(ord, "0") == 0)) ||
+                (ord && strcmp(ord, "1") == 0 && pl->S > 1);
   if (pl->S > 1) {
     pl->ml_off = kCounterBytes;
     pl->o_off = pl->ml_off + round_up((size_t)B * H * pl->S * sizeof(float2), 256);

@@ -108,7 +108,8 @@ def test_workspace_size_model(lib, monkeypatch):
 
 def _decode_ws(B, H, S, d, grid=0):
     """Counters, split (max, sum) pairs, split outputs; for grids of more than
-    1024 workgroups (with splits) also the dispatch order, one int each."""
+    1024 workgroups with at least 4 splits also the dispatch order, one int
+    each (pass grid for those)."""
     up = lambda x: (x + 255) // 256 * 256
     if grid > 1024:
         return 256 * 1024 + up(B * H * S * 8) + up(B * H * S * d * 4) + grid * 4
