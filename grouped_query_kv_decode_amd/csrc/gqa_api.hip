@@ -94,6 +94,9 @@ gqa_status check_shape(int B, int H, int G, int d, int Lmax, gqa_dtype dt) {
 //    launch of its own costs more than the in-kernel merge saves below that:
 //    at most 4% faster at 16-32 splits with 16 heads per group, up to 40%
 //    slower elsewhere).
+//  - grids of more than 1024 workgroups with at least 4 splits per sequence
+//    (several dispatch rounds) take their items largest first, in an order a
+//    small kernel sorts from the lengths on the device (GQA_ORDER=0/1).
 gqa_status make_plan(int B, int H, int G, int d, int Lmax, gqa_dtype dt, Plan *pl) {
   const int r = H / G;
   const char *force = getenv("GQA_KERNEL");
