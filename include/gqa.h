@@ -98,17 +98,20 @@ gqa_status gqa_workspace_init(void *workspace, size_t workspace_bytes, hipStream
  *             and owned by this call until the work completes on `stream`.
  *   stream    HIP stream the work is enqueued on (NULL: the null stream).
  *
- * Enqueues one kernel: a workgroup per (sequence, K/V head, context split)
- * streams that part of the cache once for all query heads of the group (with
- * few (sequence, K/V head) units, the group's heads are spread over 2 or 4
- * workgroups that read the same part); when a sequence spans several splits
- * (at most 256), the workgroup that finishes its unit last merges the split
- * results (log-sum-exp) into out.  Beyond 32 splits per sequence, above 65536
- * units, or with the environment variable GQA_MERGE=kernel, a second kernel
- * does that merge instead (beyond 32 splits one spread over sequences, heads,
- * dimensions and slices of the splits).  The
- * call allocates nothing, does not synchronise and issues no memset, so it
- * can be captured into a HIP graph (with a workspace cleared beforehand).
+ * Enqueues the decode kernel: a workgroup per (sequence, K/V head, context
+ * split) streams that part of the cache once for all query heads of the group
+ * (with few (sequence, K/V head) units, the group's heads are spread over 2
+ * or 4 workgroups that read the same part); when a sequence spans several
+ * splits (at most 256), the workgroup that finishes its unit last merges the
+ * split results (log-sum-exp) into out.  Beyond 32 splits per sequence, above
+ * 65536 units, or with the environment variable GQA_MERGE=kernel, a second
+ * kernel does that merge instead (beyond 32 splits one spread over
+ * sequences, heads, dimensions and slices of the splits).  Grids of more than
+ * 1024 workgroups with at least 4 splits per sequence are preceded by a
+ * one-workgroup kernel that orders their work items largest first (from
+ * seq_lens, on the device; the outputs do not depend on it).  The call
+ * allocates nothing, does not synchronise and issues no memset, so it can be
+ * captured into a HIP graph (with a workspace cleared beforehand).
  * NaN or Inf inside the attended positions propagate to the output.
  */
 gqa_status gqa_decode(const void *q, const void *k_cache, const void *v_cache, const int32_t *seq_lens,
