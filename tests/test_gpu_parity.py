@@ -607,3 +607,64 @@ def test_random_configurations(env, case):
     else:
         out = run_gpu(q, k, v, lt, scale)
         check(out, oracle_out(q, k, v, lt, scale), dtype, what)
+
+
+def _random_plans(n, seed):
+    """Random shapes as above, each with random plan settings: split length
+    (down to one tile, so up to ~250 splits), dispatch order forced on, the
+    wide merge forced, plain or non-temporal cache loads, head split; larger
+    batches, so that some grids exceed 1024 workgroups."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        d = int(rng.choice([64, 128]))
+        G = int(rng.choice([1, 2, 4, 8]))
+        r = int(rng.choice([1, 2, 3, 4, 8, 16, 24, 64]))
+        B = int(rng.integers(1, 40))
+        Lmax = int(rng.integers(1, 8000))
+        lens = [int(x) for x in rng.integers(0, Lmax + 1, size=B)]
+        lens[0] = Lmax
+        dtype = "bf16" if rng.random() < 0.8 else "f32"
+        window = int(rng.integers(1, Lmax + 40)) if rng.random() < 0.25 else 0
+        append = bool(rng.random() < 0.25)
+        plan = {
+            "GQA_CHUNK": int(rng.choice([32, 64, 96, 256, 512, 1000])) if rng.random() < 0.7 else None,
+            "GQA_ORDER": int(rng.choice([0, 1])) if rng.random() < 0.6 else None,
+            "GQA_FUSED_MAX_SPLITS": int(rng.choice([1, 4, 64])) if rng.random() < 0.3 else None,
+            "GQA_TEMPORAL": int(rng.choice([0, 1])) if rng.random() < 0.3 else None,
+            "GQA_HEAD_SPLIT": int(rng.choice([1, 2, 4])) if rng.random() < 0.2 else None,
+            "GQA_MERGE": "kernel" if rng.random() < 0.15 else None,
+        }
+        cases.append((i, B, G * r, G, d, Lmax, lens, dtype, window, append, plan))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_plans(48, 4242), ids=lambda c: "plan%02d" % c[0])
+def test_random_plans(env, case):
+    i, B, H, G, d, Lmax, lens, dtype, window, append, plan = case
+    env(**plan)
+    q, k, v, lt, scale = rand_case(B, H, G, d, Lmax, lens, dtype, seed=7000 + i)
+    what = "plan%02d B%d H%d G%d d%d L%d %s W%d append=%s %s" % (i, B, H, G, d, Lmax, dtype, window, append,
+                                                               {k_: v_ for k_, v_ in plan.items() if v_ is not None})
+    rows = list(range(min(B, 6)))  # the oracle on a few sequences keeps the test fast
+    if append:
+        gen = torch.Generator(DEV).manual_seed(8000 + i)
+        kn = torch.randn((B, G, d), generator=gen, device=DEV).to(k.dtype)
+        vn = torch.randn((B, G, d), generator=gen, device=DEV).to(k.dtype)
+        k0, v0 = k[:len(rows)].cpu(), v[:len(rows)].cpu()
+        out = gqa.decode_append(q, kn, vn, k, v, lt, scale, window=window)
+        torch.cuda.synchronize()
+        ref, rk, rv = oracle.decode_append(q[:len(rows)].cpu(), kn[:len(rows)].cpu(), vn[:len(rows)].cpu(), k0, v0,
+                                           lt[:len(rows)].cpu(), scale, window=window)
+        check(out[:len(rows)], ref, dtype, what)
+        bits = torch.int16 if dtype == "bf16" else torch.int32
+        nbits = np.uint16 if dtype == "bf16" else np.uint32
+        assert np.array_equal(k[:len(rows)].cpu().view(bits).numpy().view(nbits), rk.view(nbits)), what
+        assert np.array_equal(v[:len(rows)].cpu().view(bits).numpy().view(nbits), rv.view(nbits)), what
+    else:
+        out = gqa.decode_window(q, k, v, lt, scale, window) if window else gqa.decode(q, k, v, lt, scale)
+        torch.cuda.synchronize()
+        ref = oracle.decode(q[:len(rows)].cpu(), k[:len(rows)].cpu(), v[:len(rows)].cpu(), lt[:len(rows)].cpu(),
+                            scale, window=window)
+        check(out[:len(rows)], ref, dtype, what)
+
