@@ -46,7 +46,7 @@ def env(monkeypatch):
             else:
                 monkeypatch.setenv(k, str(v))
     set_(GQA_KERNEL=None, GQA_CHUNK=None, GQA_TARGET_WGS=None, GQA_MAX_CHUNK=None, GQA_MERGE=None, GQA_WAVES=None,
-         GQA_CONTIG=None, GQA_HEAD_SPLIT=None, GQA_FUSED_MAX_SPLITS=None, GQA_ORDER=None)
+         GQA_CONTIG=None, GQA_HEAD_SPLIT=None, GQA_FUSED_MAX_SPLITS=None, GQA_ORDER=None, GQA_TEMPORAL=None)
     return set_
 
 
