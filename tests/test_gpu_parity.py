@@ -228,6 +228,30 @@ def test_dispatch_order(env, dtype, kernel):
     assert torch.equal(k1.view(bits), k0.view(bits)) and torch.equal(v1.view(bits), v0.view(bits))
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_dispatch_order_large_batch(env, dtype):
+    """More sequences than the order kernel stages in LDS (4096): it then reads
+    each item's length from memory.  Outputs are bit-equal with the order
+    forced off, forced on and left to the plan (on: 50,000 workgroups of 5
+    splits), and sampled sequences - both sides of the 4096 boundary, empty
+    ones included - agree with the oracle."""
+    B, H, G, d, L = 5000, 8, 2, 64, 160
+    gen = torch.Generator().manual_seed(81)
+    lens = [int(x) for x in torch.randint(0, L + 1, (B,), generator=gen)]
+    lens[:3] = [L, 0, 1]
+    lens[4096] = L
+    lens[-1] = 33
+    q, k, v, lt, scale = rand_case(B, H, G, d, L, lens, dtype, seed=82)
+    env(GQA_CHUNK=32, GQA_ORDER=0)
+    ref = run_gpu(q, k, v, lt, scale).clone()
+    for order in (1, None):
+        env(GQA_ORDER=order)
+        assert torch.equal(run_gpu(q, k, v, lt, scale), ref), "order %s" % order
+    picks = [int(x) for x in torch.randint(0, B, (24,), generator=gen)]
+    rows = sorted(set([0, 1, 2, 4095, 4096, 4097, B - 1] + picks))
+    check(ref[rows], oracle_out(q, k, v, lt, scale, rows=rows), dtype, "B5000 ordered, sampled rows")
+
+
 def test_very_long_sequence(env):
     """2,097,152 positions: the 4096-position split cap gives 512 splits (more
     than the planner's usual 256), merged by the wide kernel 16 per slice."""
