@@ -294,18 +294,27 @@ gqa_status packed_impl(const void *x, const void *wp, void *const y[3], const in
   p.M = M;
   p.K = K;
   p.N = N;
-  // 8 waves x 2 blocks per chunk up to 512 strips, 4 x 2 beyond (measured
-  // best on the Mistral-7B projections and a 28672-wide one); GQA_LINEAR_WAVES
-  // and GQA_LINEAR_TPI override.
-  const int nw_def = N / 16 <= 512 ? 8 : 4;
-  const int nw = env_int("GQA_LINEAR_WAVES", nw_def) == 8 ? 8 : 4;
+  // One token tile: 2 or 4 strips per workgroup where one strip each would
+  // leave more than ~1.5 workgroups per compute unit, as long as at least
+  // 192 workgroups remain (each workgroup reads all of x, so fewer and wider
+  // ones read less of it: [4096 x 6144] 12.3 -> 10.7 us with 2 strips);
+  // K of 4, 8 or 16 chunks runs the unrolled kernel (measured 0.5-1 us
+  // faster than the loop: [4096 x 4096] 7.9 us).  GQA_LINEAR_STRIPS=1|2|4
+  // and GQA_LINEAR_UNROLL=0 override.
   const int tb = ceil_div(M, 16) > 2 ? 4 : ceil_div(M, 16);
-  const int max_tpi = 32 / (tb * nw);  // two x chunks staged in LDS: TB*NW*TPI <= 32
-  int tpi = env_int("GQA_LINEAR_TPI", 2);
-  if (tpi != 1 && tpi != 2 && tpi != 4 && tpi != 8) tpi = 2;
-  if (tpi > max_tpi) tpi = max_tpi;
-  const int pd = 2;
-  const hipError_t e = gqa::launch_linear_packed(p, nw, tpi, pd, stream);
+  const int nstrips = N / 16;
+  int sw = 1;
+  if (tb == 1) {
+    for (int cand : {4, 2})
+      if (sw == 1 && nstrips % cand == 0 && nstrips / cand >= 192) sw = cand;
+    const int sw_env = env_int("GQA_LINEAR_STRIPS", 0);
+    if ((sw_env == 1 || sw_env == 2 || sw_env == 4) && nstrips % sw_env == 0) sw = sw_env;
+  }
+  const int kc = gqa::linear_packed_chunk_blocks(tb, sw);
+  const int nch = (K / 32) % kc == 0 ? K / 32 / kc : 0;
+  const bool unroll = tb == 1 && sw <= 2 && (nch == 4 || nch == 8 || nch == 16) &&
+                      !(getenv("GQA_LINEAR_UNROLL") && strcmp(getenv("GQA_LINEAR_UNROLL"), "0") == 0);
+  const hipError_t e = gqa::launch_linear_packed(p, tb, sw, unroll ? nch : 0, stream);
   return e == hipSuccess ? GQA_OK : hip_fail(e);
 }
 

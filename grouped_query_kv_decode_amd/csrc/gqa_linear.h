@@ -20,7 +20,11 @@ struct LinearParams {
 };
 
 hipError_t launch_linear(const LinearParams &p, int NW, int TPI, unsigned grid, hipStream_t stream);
-hipError_t launch_linear_packed(const LinearParams &p, int NW, int TPI, int PD, hipStream_t stream);
+// tb: token tiles (1, 2 or 4); sw: strips per workgroup; nch: chunks of
+// linear_packed_chunk_blocks(tb, sw) k-blocks unrolled at compile time (K must
+// then equal nch chunks), 0 for the loop over any K.
+hipError_t launch_linear_packed(const LinearParams &p, int tb, int sw, int nch, hipStream_t stream);
+int linear_packed_chunk_blocks(int tb, int sw);
 hipError_t launch_pack_weight(const void *w, void *w_packed, int K, int N, hipStream_t stream);
 
 }  // namespace gqa

@@ -17,11 +17,11 @@
 // would have every workgroup reading at the same offset of its own strip, a
 // fixed stride apart.
 //
-// Kernel: one workgroup per 16-column strip streams the strip over all of K
-// (no split of k, so no partial sums leave the workgroup); its waves take
-// blocks in turn, TPI at a time with all loads issued before the first MFMA,
-// and are summed through LDS in wave order.  x, the B operand, is small and
-// every workgroup reads all of it (from L2), staged through LDS.
+// Kernel: one workgroup per 1, 2 or 4 adjacent 16-column strips streams them
+// over all of K (no split of k, so no partial sums leave the workgroup); its
+// waves take blocks in turn and are summed through LDS in wave order.  x, the
+// B operand, is small and every workgroup reads all of it (from L2), staged
+// through LDS; wider workgroups read less x in total.
 #include "gqa_device.h"
 #include "gqa_linear.h"
 
@@ -54,64 +54,78 @@ __device__ __forceinline__ void store4(const LinearParams &p, int row, int col, 
   *reinterpret_cast<bf16x4 *>(dst) = o;
 }
 
-template <int TB, int NW, int TPI, int PD>
+// Workgroup: SW adjacent strips (16 SW output columns) over all of K.  Its
+// NW waves take the blocks of a chunk of KC = NW*TPI consecutive k-blocks
+// in turn (wave w: blocks w, w+NW, ...), each block feeding SW MFMAs (one per
+// strip) with the same x operand.
+//
+// Pipeline: a ring of PD chunks - the weights and x of chunk i are requested
+// PD-1 chunks before chunk i is multiplied.  Every chunk issues the same
+// loads (addresses past the end are clamped in bounds and their data never
+// used), so the wait before a chunk's products covers that chunk's loads
+// only and leaves the later ones in flight; with conditional loads the
+// compiler drains every load at each chunk, and the kernel then runs at one
+// memory latency per chunk.  NCH > 0 unrolls all NCH chunks at compile time
+// (K = NCH*KC*32): no loop back edge, whose register copies would also force
+// a full drain; NCH = 0 loops over any K.
+template <int TB, int NW, int TPI, int SW, int PD, int NCH>
 __global__ __launch_bounds__(64 * NW) void linear_packed(LinearParams p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane >> 4, nn = lane & 15;
-  const int nb = blockIdx.x;
-  const int kblocks = p.K / 32;
-  // lane's 16 bytes of block (kb = 0) of this strip; blocks of a strip are N/16 KiB apart
   const int nstrips = p.N / 16;
-  const __bf16 *wl = p.w + (size_t)nb * 512 + lane * 8;
+  const int nb0 = blockIdx.x * SW;  // first strip
+  const int kblocks = p.K / 32;
+  // lane's 16 bytes of block (kb = 0) of strip nb0; blocks of one strip are N/16 KiB apart
+  const __bf16 *wl = p.w + (size_t)nb0 * 512 + lane * 8;
 
-  // x is staged through LDS a chunk of KC blocks (KC*32 values of k) at a
-  // time: read from memory as whole row segments, then each lane takes its
-  // B operand (token nn, 8 values of k) from LDS.  Read straight from memory
+  // x staged through LDS a chunk at a time: read from memory as whole row
+  // segments (16-byte pieces, XPT per thread), then each lane takes its B
+  // operand (token nn, 8 values of k) from LDS.  Read straight from memory
   // the operand would touch 16 half-used cache lines per wave-wide load.
-  // Software pipeline: while chunk i is multiplied, x of chunk i+1 and the
-  // weights of chunks i+1 .. i+PD-1 are in flight (PD register sets for the
-  // weights, two LDS buffers for x, one barrier per chunk).
   constexpr int KC = NW * TPI;
-  constexpr int ROWB = KC * 64 + 16;         // bytes per token row (+16: spreads the LDS banks)
-  constexpr int PPR = KC * 4;                // 16-byte pieces per row
-  constexpr int XPT = (TB * 16 * PPR + 64 * NW - 1) / (64 * NW);  // pieces per thread
+  constexpr int ROWB = KC * 64 + 16;  // bytes per token row (+16: spreads the LDS banks)
+  constexpr int PPR = KC * 4;         // 16-byte pieces per row
+  constexpr int XPT = TB * 16 * PPR / (64 * NW);
+  static_assert(XPT * 64 * NW == TB * 16 * PPR, "x pieces split evenly over the threads");
   constexpr int BUFB = TB * 16 * ROWB;
   __shared__ __attribute__((aligned(16))) unsigned char xs[2 * BUFB];
 
-  f32x4 acc[TB];
+  f32x4 acc[SW][TB];
 #pragma unroll
-  for (int tb = 0; tb < TB; ++tb) acc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < SW; ++s)
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) acc[s][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // Rows past M repeat row M-1 (they only feed outputs past M, never
+  // stored); pieces past the last k-block repeat it (never read from LDS).
   auto load_x = [&](u32x4 (&xr)[XPT], int kb0) {
-    const int nkb = min(KC, kblocks - kb0);
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
       const int idx = threadIdx.x + i * 64 * NW;
-      const int row = idx / PPR, pc = idx % PPR;
-      xr[i] = (row < p.M && pc < nkb * 4)
-                  ? *reinterpret_cast<const u32x4 *>(p.x + (size_t)row * p.K + kb0 * 32 + pc * 8)
-                  : u32x4{0u, 0u, 0u, 0u};
+      const int row = min(idx / PPR, p.M - 1), pc = idx % PPR;
+      const int kb = min(kb0 + pc / 4, kblocks - 1);
+      xr[i] = *reinterpret_cast<const u32x4 *>(p.x + (size_t)row * p.K + kb * 32 + (pc % 4) * 8);
     }
   };
-  // this wave's weight blocks of a chunk; past the end: re-read the last
-  // block (in bounds), skipped in the products
-  auto load_w = [&](u32x4 (&a)[TPI], int kb0) {
+  // this wave's blocks of a chunk, one per strip; past the end: the last
+  // block again (in bounds, skipped in the products)
+  auto load_w = [&](u32x4 (&a)[TPI][SW], int kb0) {
 #pragma unroll
     for (int j = 0; j < TPI; ++j) {
       const int kb = min(kb0 + wave + j * NW, kblocks - 1);
-      a[j] = stream_load(reinterpret_cast<const u32x4 *>(wl + (size_t)kb * nstrips * 512));
+#pragma unroll
+      for (int s = 0; s < SW; ++s)
+        a[j][s] = stream_load(reinterpret_cast<const u32x4 *>(wl + ((size_t)kb * nstrips + s) * 512));
     }
   };
   auto store_x = [&](const u32x4 (&xr)[XPT], unsigned char *buf) {
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
       const int idx = threadIdx.x + i * 64 * NW;
-      const int row = idx / PPR, pc = idx % PPR;
-      if (row < TB * 16) *reinterpret_cast<u32x4 *>(buf + row * ROWB + pc * 16) = xr[i];
+      *reinterpret_cast<u32x4 *>(buf + (idx / PPR) * ROWB + (idx % PPR) * 16) = xr[i];
     }
   };
-  auto products = [&](const u32x4 (&a)[TPI], const unsigned char *buf, int kb0) {
-    const int nkb = min(KC, kblocks - kb0);
+  auto products = [&](const u32x4 (&a)[TPI][SW], const unsigned char *buf, int nkb) {
 #pragma unroll
     for (int j = 0; j < TPI; ++j) {
       const int kl = wave + j * NW;  // block within the chunk
@@ -119,48 +133,62 @@ __global__ __launch_bounds__(64 * NW) void linear_packed(LinearParams p) {
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb) {
         const u32x4 b = *reinterpret_cast<const u32x4 *>(buf + (tb * 16 + nn) * ROWB + (kl * 32 + 8 * c) * 2);
-        acc[tb] = mfma(a[j], b, acc[tb]);
+#pragma unroll
+        for (int s = 0; s < SW; ++s) acc[s][tb] = mfma(a[j][s], b, acc[s][tb]);
       }
     }
   };
 
-  u32x4 xr[XPT], a[PD][TPI];
-  load_x(xr, 0);
+  u32x4 xr[PD][XPT], a[PD][TPI][SW];
 #pragma unroll
-  for (int d = 0; d < PD - 1; ++d)
-    if (d * KC < kblocks) load_w(a[d], d * KC);
-  int buf = 0;
-  for (int kb0 = 0; kb0 < kblocks; kb0 += PD * KC) {
+  for (int d = 0; d < PD - 1; ++d) {
+    load_x(xr[d], d * KC);
+    load_w(a[d], d * KC);
+  }
+  if constexpr (NCH > 0) {
 #pragma unroll
-    for (int ph = 0; ph < PD; ++ph) {
-      const int kc = kb0 + ph * KC;  // this chunk; its weights are in a[ph]
-      if (kc >= kblocks) break;
-      store_x(xr, xs + buf * BUFB);
-      if (kc + KC < kblocks) load_x(xr, kc + KC);
-      if (kc + (PD - 1) * KC < kblocks) load_w(a[(ph + PD - 1) % PD], kc + (PD - 1) * KC);
+    for (int i = 0; i < NCH; ++i) {
+      if (i + PD - 1 < NCH) {
+        load_x(xr[(i + PD - 1) % PD], (i + PD - 1) * KC);
+        load_w(a[(i + PD - 1) % PD], (i + PD - 1) * KC);
+      }
+      store_x(xr[i % PD], xs + (i & 1) * BUFB);
       __syncthreads();
-      products(a[ph], xs + buf * BUFB, kc);
-      buf ^= 1;
+      products(a[i % PD], xs + (i & 1) * BUFB, KC);
+    }
+  } else {
+    int buf = 0;
+    for (int kb0 = 0; kb0 < kblocks; kb0 += PD * KC) {
+#pragma unroll
+      for (int ph = 0; ph < PD; ++ph) {
+        const int kc = kb0 + ph * KC;  // this chunk; its x and weights are in slot ph
+        if (kc >= kblocks) break;
+        load_x(xr[(ph + PD - 1) % PD], kc + (PD - 1) * KC);
+        load_w(a[(ph + PD - 1) % PD], kc + (PD - 1) * KC);
+        store_x(xr[ph], xs + buf * BUFB);
+        __syncthreads();
+        products(a[ph], xs + buf * BUFB, min(KC, kblocks - kc));
+        buf ^= 1;
+      }
     }
   }
 
-  // acc[tb][i] of lane (c, nn) = y[token tb*16 + nn][column 16nb + 4c + i]
+  // acc[s][tb][i] of lane (c, nn) = y[token tb*16 + nn][column 16 (nb0 + s) + 4c + i]
   // of this wave's blocks.  Sum the waves in wave order.
-  __shared__ f32x4 sm[NW > 1 ? NW - 1 : 1][TB][64];
-  if (wave > 0) {
+  __shared__ f32x4 sm[NW][SW][TB][64];
 #pragma unroll
-    for (int tb = 0; tb < TB; ++tb) sm[wave - 1][tb][lane] = acc[tb];
-  }
+  for (int s = 0; s < SW; ++s)
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) sm[wave][s][tb][lane] = acc[s][tb];
   __syncthreads();
-  if (wave != 0) return;
+  for (int it = threadIdx.x; it < SW * TB * 64; it += 64 * NW) {
+    const int l = it % 64, tb = (it / 64) % TB, s = it / (64 * TB);
+    const int row = tb * 16 + (l & 15);
+    if (row >= p.M) continue;
+    f32x4 t = sm[0][s][tb][l];
 #pragma unroll
-  for (int w = 1; w < NW; ++w)
-#pragma unroll
-    for (int tb = 0; tb < TB; ++tb) acc[tb] += sm[w - 1][tb][lane];
-#pragma unroll
-  for (int tb = 0; tb < TB; ++tb) {
-    const int row = tb * 16 + nn;
-    if (row < p.M) store4(p, row, nb * 16 + 4 * c, acc[tb]);
+    for (int w = 1; w < NW; ++w) t += sm[w][s][tb][l];
+    store4(p, row, 16 * (nb0 + s) + 4 * (l >> 4), t);
   }
 }
 
@@ -182,53 +210,48 @@ __global__ __launch_bounds__(256) void pack_kernel(const __bf16 *__restrict__ w,
   *reinterpret_cast<u16x8 *>(wp + g * 8) = v;
 }
 
-// Two x chunks in LDS, TB*16 rows of NW*TPI*64 bytes each: at most ~66 KiB.
-// PD*TPI weight operands per lane in registers.
-template <int TB, int NW, int TPI, int PD>
+template <int TB, int NW, int TPI, int SW, int PD, int NCH>
 hipError_t launch_one(const LinearParams &p, hipStream_t stream) {
-  if constexpr (TB * NW * TPI > 32 || PD * TPI > 16) {
-    return hipErrorInvalidValue;
-  } else {
-    hipLaunchKernelGGL((linear_packed<TB, NW, TPI, PD>), dim3(p.N / 16), dim3(64 * NW), 0, stream, p);
-    return hipGetLastError();
-  }
-}
-
-template <int TB, int TPI, int PD>
-hipError_t launch_nw(const LinearParams &p, int NW, hipStream_t stream) {
-  return NW == 8 ? launch_one<TB, 8, TPI, PD>(p, stream) : launch_one<TB, 4, TPI, PD>(p, stream);
-}
-
-template <int TPI, int PD>
-hipError_t launch_tb(const LinearParams &p, int NW, hipStream_t stream) {
-  switch ((p.M + 15) / 16) {
-    case 1: return launch_nw<1, TPI, PD>(p, NW, stream);
-    case 2: return launch_nw<2, TPI, PD>(p, NW, stream);
-    case 3:
-    case 4: return launch_nw<4, TPI, PD>(p, NW, stream);
-    default: return hipErrorInvalidValue;
-  }
-}
-
-template <int PD>
-hipError_t launch_tpi(const LinearParams &p, int NW, int TPI, hipStream_t stream) {
-  switch (TPI) {
-    case 1: return launch_tb<1, PD>(p, NW, stream);
-    case 2: return launch_tb<2, PD>(p, NW, stream);
-    case 4: return launch_tb<4, PD>(p, NW, stream);
-    case 8: return launch_tb<8, PD>(p, NW, stream);
-    default: return hipErrorInvalidValue;
-  }
+  hipLaunchKernelGGL((linear_packed<TB, NW, TPI, SW, PD, NCH>), dim3(p.N / 16 / SW), dim3(64 * NW), 0, stream, p);
+  return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_linear_packed(const LinearParams &p, int NW, int TPI, int PD, hipStream_t stream) {
-  // prefetch distance 2 (one chunk ahead) measured best; deeper rings are
-  // available to the template but not instantiated
-  return PD == 2 ? launch_tpi<2>(p, NW, TPI, stream) : hipErrorInvalidValue;
-}
+// The instantiated shapes (x chunks of TB*16 rows x KC blocks staged twice in
+// LDS, at most ~68 KiB; the wave partial sums NW*SW*TB KiB):
+//   one token tile: 1 strip, 4 waves x 4 blocks, ring of 3 (unrolled) or 2;
+//                   2 strips, 8 waves x 2 blocks, ring of 4 (unrolled) or 2;
+//                   4 strips, 4 waves x 1 block, ring of 2;
+//   two / four token tiles: 1 strip, 4 waves x 4 / 2 blocks, ring of 2.
+// Unrolled for K = 2048, 4096 and 8192 (4, 8 and 16 chunks of 16 blocks).
+int linear_packed_chunk_blocks(int tb, int sw) { return tb == 4 ? 8 : (sw == 4 ? 4 : 16); }
 
+hipError_t launch_linear_packed(const LinearParams &p, int tb, int sw, int nch, hipStream_t stream) {
+  if (tb == 1 && sw == 1) {
+    switch (nch) {
+      case 0: return launch_one<1, 4, 4, 1, 2, 0>(p, stream);
+      case 4: return launch_one<1, 4, 4, 1, 3, 4>(p, stream);
+      case 8: return launch_one<1, 4, 4, 1, 3, 8>(p, stream);
+      case 16: return launch_one<1, 4, 4, 1, 3, 16>(p, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  if (tb == 1 && sw == 2) {
+    switch (nch) {
+      case 0: return launch_one<1, 8, 2, 2, 2, 0>(p, stream);
+      case 4: return launch_one<1, 8, 2, 2, 4, 4>(p, stream);
+      case 8: return launch_one<1, 8, 2, 2, 4, 8>(p, stream);
+      case 16: return launch_one<1, 8, 2, 2, 4, 16>(p, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  if (nch != 0) return hipErrorInvalidValue;
+  if (tb == 1 && sw == 4) return launch_one<1, 4, 1, 4, 2, 0>(p, stream);
+  if (tb == 2 && sw == 1) return launch_one<2, 4, 4, 1, 2, 0>(p, stream);
+  if (tb == 4 && sw == 1) return launch_one<4, 4, 2, 1, 2, 0>(p, stream);
+  return hipErrorInvalidValue;
+}
 hipError_t launch_pack_weight(const void *w, void *w_packed, int K, int N, hipStream_t stream) {
   const size_t groups = (size_t)K * N / 8;
   const unsigned grid = (unsigned)((groups + 255) / 256);

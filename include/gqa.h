@@ -210,9 +210,9 @@ gqa_status gqa_pack_weight(const void *w, void *w_packed, int K, int N, gqa_dtyp
 
 /*
  * gqa_linear over a packed weight (gqa_pack_weight): y[M, N] = x[M, K] @ W.
- * One workgroup per 16-column strip reads the strip once over all of K, so
- * no workspace is needed and each output is one binary32 sum (in a fixed
- * order) rounded once to bfloat16.
+ * Each workgroup reads 1, 2 or 4 adjacent 16-column strips once over all of
+ * K, so no workspace is needed and each output is one binary32 sum (in an
+ * order fixed by the shape) rounded once to bfloat16.
  *   x [M, K], y [M, N] bfloat16 row-major, 16-byte aligned; M in 0..64
  *   (0 is a no-op); K a multiple of 32; N a multiple of 16; dtype GQA_BF16.
  * Status codes as for gqa_linear.

@@ -164,23 +164,31 @@ def test_pack_weight_layout(shape):
 PACKED_CASES = [
     # (M, K, N)
     (1, 32, 16),             # one block
-    (5, 96, 48),             # ragged tokens, three strips
-    (16, 4096, 6144),        # fused q/k/v projection, d_model 4096, H 32, G 8, d 128
-    (16, 4096, 4096),        # output projection of the same layer
+    (5, 96, 48),             # ragged tokens, three strips, a partial chunk
+    (4, 1056, 64),           # two whole chunks and a partial one (loop)
+    (16, 4096, 6144),        # fused q/k/v projection, d_model 4096, H 32, G 8, d 128 (2 strips, unrolled)
+    (16, 4096, 4096),        # output projection of the same layer (1 strip, unrolled)
+    (16, 2048, 4096),        # 4 unrolled chunks
+    (8, 2048, 6144),         # 2 strips, 4 unrolled chunks
+    (1, 8192, 6144),         # 2 strips, 16 unrolled chunks, one token
+    (12, 4096, 8192),        # 4 strips per workgroup
     (17, 1024, 272),         # two token tiles
     (33, 512, 640),          # three token tiles (rounded up to four)
     (64, 4096, 128),         # most tokens
-    (3, 8192, 1024),
+    (3, 8192, 1024),         # 16 unrolled chunks
     (2, 4096, 1088),         # fused projection of H 16, G 1, d 64
 ]
 
 
 @pytest.mark.parametrize("case", PACKED_CASES, ids=lambda c: "M%d_K%d_N%d" % c)
-@pytest.mark.parametrize("plan", [(None, None), ("4", "4"), ("8", "16"), ("8", "8")], ids=["default", "w4t4",
-                                                                                          "w8t16", "w8t8"])
+@pytest.mark.parametrize("plan", [(None, None), ("1", None), ("2", None), ("4", None), (None, "0"), ("2", "0")],
+                         ids=["default", "strips1", "strips2", "strips4", "loop", "strips2_loop"])
 def test_linear_packed_parity(monkeypatch, case, plan):
+    """Every kernel variant of the packed projection (strips per workgroup,
+    unrolled or looped chunks; strip counts that do not divide the output
+    fall back to one) against the oracle."""
     M, K, N = case
-    for name, v in (("GQA_LINEAR_WAVES", plan[0]), ("GQA_LINEAR_TPI", plan[1])):
+    for name, v in (("GQA_LINEAR_STRIPS", plan[0]), ("GQA_LINEAR_UNROLL", plan[1])):
         if v is None:
             monkeypatch.delenv(name, raising=False)
         else:
