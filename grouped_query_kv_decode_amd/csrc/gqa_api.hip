@@ -105,6 +105,29 @@ gqa_status make_plan(int B, int H, int G, int d, int Lmax, gqa_dtype dt, Plan *p
   if (force && strcmp(force, "mfma") == 0 && dt == GQA_BF16 && r <= 64) kind = KIND_MFMA;
   pl->kind = kind;
   pl->NW = 4;
+  const int target = env_int("GQA_TARGET_WGS", 256);
+  const int max_chunk = env_int("GQA_MAX_CHUNK", 4096);
+  const int chunk_env = env_int("GQA_CHUNK", 0);
+  // Split length for a grid of `units` (b, g, head chunk) units.
+  auto chunk_for = [&](long units) {
+    int chunk = chunk_env;
+    if (chunk == 0) {
+      long S = (target + units - 1) / units;
+      if (S < 1) S = 1;
+      chunk = (int)round_up((size_t)ceil_div(Lmax, S), 32);
+      // Floors: the matrix-core kernel's 4 waves take 8 tiles of 32 positions
+      // per 256 (shorter splits cost more in epilogue and merge than they
+      // gain), the VALU kernel's rows are shorter; and at most kMaxSplits
+      // splits per sequence (beyond kMaxFusedSplits merged by a second kernel).
+      const int min_chunk = kind == KIND_MFMA ? 256 : 32;
+      if (chunk < min_chunk) chunk = min_chunk;
+      const int min_for_merge = (int)round_up((size_t)ceil_div(Lmax, kMaxSplits), 32);
+      if (chunk < min_for_merge) chunk = min_for_merge;
+      if (chunk > max_chunk) chunk = max_chunk;
+    }
+    return chunk > Lmax ? Lmax : chunk;
+  };
+  const int fused_max = env_int("GQA_FUSED_MAX_SPLITS", kMaxFusedSplits);
   if (kind == KIND_MFMA) {
     const int hb = (r + 15) / 16;
     const int hb_all = hb <= 1 ? 1 : (hb <= 2 ? 2 : 4);
@@ -112,10 +135,36 @@ gqa_status make_plan(int B, int H, int G, int d, int Lmax, gqa_dtype dt, Plan *p
     // units than compute units: a workgroup's tile loop serves each of its
     // head blocks in turn, so with few units the loop, not HBM, sets the pace.
     int hc = ((long)B * G < 256) ? hb_all : 1;
+    auto fit = [&](int h) {  // no chunk without heads
+      while (h > 1 && (h - 1) * (hb_all / h) * 16 >= r) h /= 2;
+      return h;
+    };
+    hc = fit(hc);
+    if (hc == 4) {
+      // Every head chunk reads the whole slab, through a compute unit's
+      // memory path (~35 GB/s, from L2 or HBM alike), and the in-kernel merge
+      // is one workgroup reading heads x splits partials.  Two chunks instead
+      // of four halve the first; four keep the splits, and so the merge,
+      // small.  Estimate both in KiB through the slowest compute unit: its
+      // workgroups' slabs, plus the fused merge (serial, at the end: x4) or
+      // the wide merge kernel's launch (~128 KiB worth).  Measured (bf16, 64
+      // heads per K/V head): 2 chunks B64 d64 L4096 29.0 -> 23.2 us,
+      // B2 d128 L32768 32.9 -> 22.8 us, B128 d128 L1024 26.3 -> 21.6 us;
+      // 4 chunks B4 d64 L8192 12.8 (19.6 with 2), B8 d128 L8192 21.8 (26.5).
+      auto cost = [&](int h) {
+        const long units = (long)B * G * h;
+        const int chunk = chunk_for(units);
+        const long S = ceil_div(Lmax, chunk);
+        const long rounds = (units * S + 255) / 256;
+        const double slab_kib = (double)chunk * d * 4 / 1024 * rounds;
+        const int heads = (hb_all / h) * 16 < r ? (hb_all / h) * 16 : r;
+        const double merge_kib = S <= 1 ? 0.0 : (S > fused_max ? 128.0 : 4.0 * heads * S * (d + 2) * 4 / 1024);
+        return slab_kib + merge_kib;
+      };
+      if (cost(2) < cost(4)) hc = 2;
+    }
     const int hc_env = env_int("GQA_HEAD_SPLIT", 0);
-    if (hc_env == 1 || hc_env == 2 || hc_env == 4) hc = hc_env;
-    if (hc > hb_all) hc = hb_all;
-    while (hc > 1 && (hc - 1) * (hb_all / hc) * 16 >= r) hc /= 2;  // no chunk without heads
+    if (hc_env == 1 || hc_env == 2 || hc_env == 4) hc = fit(hc_env > hb_all ? hb_all : hc_env);
     pl->HC = hc;
     pl->HB = hb_all / hc;
     pl->NW = 4;  // chosen below, once the split length is known
@@ -126,24 +175,7 @@ gqa_status make_plan(int B, int H, int G, int d, int Lmax, gqa_dtype dt, Plan *p
     pl->HB = 0;
   }
   const long units = (long)B * G * pl->HC;
-  const int target = env_int("GQA_TARGET_WGS", 256);
-  const int max_chunk = env_int("GQA_MAX_CHUNK", 4096);
-  int chunk = env_int("GQA_CHUNK", 0);
-  if (chunk == 0) {
-    long S = (target + units - 1) / units;
-    if (S < 1) S = 1;
-    chunk = (int)round_up((size_t)ceil_div(Lmax, S), 32);
-    // Floors: the matrix-core kernel's 4 waves take 8 tiles of 32 positions
-    // per 256 (shorter splits cost more in epilogue and merge than they
-    // gain), the VALU kernel's rows are shorter; and at most kMaxSplits
-    // splits per sequence (beyond kMaxFusedSplits merged by a second kernel).
-    const int min_chunk = kind == KIND_MFMA ? 256 : 32;
-    if (chunk < min_chunk) chunk = min_chunk;
-    const int min_for_merge = (int)round_up((size_t)ceil_div(Lmax, kMaxSplits), 32);
-    if (chunk < min_for_merge) chunk = min_for_merge;
-    if (chunk > max_chunk) chunk = max_chunk;
-  }
-  if (chunk > Lmax) chunk = Lmax;
+  const int chunk = chunk_for(units);
   pl->chunk = chunk;
   if (kind == KIND_MFMA) {
     // 4 waves (measured best on every workload with the non-temporal cache

@@ -134,6 +134,14 @@ def test_split_plan_model(lib, monkeypatch):
         (1, 8, 2, 64, 8192, F32, 128),        # VALU, 2 units: 64-position splits
         (1, 8, 1, 128, 131072, BF16, 256),    # one unit, long: 512-position splits (256 WGs)
         (1, 8, 1, 128, 262144, F32, 256),     # at most 256 splits: 1024 positions
+        # 64 heads per K/V head: 2 or 4 head chunks, whichever moves fewer
+        # bytes through the busiest compute unit (slabs + merge)
+        (32, 64, 1, 64, 2048, BF16, 4),       # 2 chunks: 64 units x 512 positions
+        (64, 64, 1, 64, 4096, BF16, 2),       # 2 chunks (4 would read whole slabs: 1 split)
+        (32, 128, 2, 128, 4096, BF16, 2),     # 2 chunks
+        (4, 64, 1, 64, 8192, BF16, 16),       # 4 chunks (2 would merge 32 heads x 32 splits)
+        (8, 64, 1, 128, 8192, BF16, 8),       # 4 chunks
+        (2, 64, 1, 128, 32768, BF16, 64),     # 2 chunks, 64 splits for the wide merge
     ]
     for B, H, G, d, L, dt, S, *grid in cases:
         assert lib.gqa_decode_workspace_size(B, H, G, d, L, dt) == _decode_ws(B, H, S, d, *grid), (B, H, G, d, L, dt, S)
