@@ -140,17 +140,21 @@ gqa_status make_plan(int B, int H, int G, int d, int Lmax, gqa_dtype dt, Plan *p
       return h;
     };
     hc = fit(hc);
-    if (hc == 4) {
+    if (hc > 1) {
       // Every head chunk reads the whole slab, through a compute unit's
       // memory path (~35 GB/s, from L2 or HBM alike), and the in-kernel merge
-      // is one workgroup reading heads x splits partials.  Two chunks instead
-      // of four halve the first; four keep the splits, and so the merge,
-      // small.  Estimate both in KiB through the slowest compute unit: its
-      // workgroups' slabs, plus the fused merge (serial, at the end: x4) or
-      // the wide merge kernel's launch (~128 KiB worth).  Measured (bf16, 64
-      // heads per K/V head): 2 chunks B64 d64 L4096 29.0 -> 23.2 us,
-      // B2 d128 L32768 32.9 -> 22.8 us, B128 d128 L1024 26.3 -> 21.6 us;
-      // 4 chunks B4 d64 L8192 12.8 (19.6 with 2), B8 d128 L8192 21.8 (26.5).
+      // is one workgroup reading heads x splits partials.  Fewer chunks read
+      // less; more chunks keep the splits, and so the merge, small.  Estimate
+      // both candidates (1 or 2 chunks for two head blocks, 2 or 4 for four)
+      // in KiB through the slowest compute unit: its workgroups' slabs, plus,
+      // when the sequence is split, the tail of the split protocol (partial
+      // stores, arrival, merge: ~128 KiB worth) and the fused merge (serial,
+      // at the end: x4) or the wide merge kernel's launch (~128 KiB worth).
+      // Picks the faster plan on 21 of 22 measured shapes (bf16; 64 heads per
+      // K/V head: 2 chunks B64 d64 L4096 29.0 -> 23.2 us, B2 d128 L32768
+      // 32.9 -> 22.8 us; 4 chunks B4 d64 L8192 12.8 us (19.6 with 2); 32
+      // heads: 1 chunk B4 d128 L16384 25.1 -> 19.0 us, B1 d128 L131072
+      // 28.2 -> 23.2 us; 2 chunks B8 d64 L8192 13.1 us (19.5 with 1)).
       auto cost = [&](int h) {
         const long units = (long)B * G * h;
         const int chunk = chunk_for(units);
@@ -158,10 +162,11 @@ gqa_status make_plan(int B, int H, int G, int d, int Lmax, gqa_dtype dt, Plan *p
         const long rounds = (units * S + 255) / 256;
         const double slab_kib = (double)chunk * d * 4 / 1024 * rounds;
         const int heads = (hb_all / h) * 16 < r ? (hb_all / h) * 16 : r;
-        const double merge_kib = S <= 1 ? 0.0 : (S > fused_max ? 128.0 : 4.0 * heads * S * (d + 2) * 4 / 1024);
-        return slab_kib + merge_kib;
+        if (S <= 1) return slab_kib;
+        return slab_kib + 128.0 + (S > fused_max ? 128.0 : 4.0 * heads * S * (d + 2) * 4 / 1024);
       };
-      if (cost(2) < cost(4)) hc = 2;
+      const int other = fit(hc / 2);  // at most two head blocks per workgroup (four measured slower)
+      if (other != hc && hb_all / other <= 2 && cost(other) < cost(hc)) hc = other;
     }
     const int hc_env = env_int("GQA_HEAD_SPLIT", 0);
     if (hc_env == 1 || hc_env == 2 || hc_env == 4) hc = fit(hc_env > hb_all ? hb_all : hc_env);

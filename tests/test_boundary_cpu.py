@@ -142,6 +142,10 @@ def test_split_plan_model(lib, monkeypatch):
         (4, 64, 1, 64, 8192, BF16, 16),       # 4 chunks (2 would merge 32 heads x 32 splits)
         (8, 64, 1, 128, 8192, BF16, 8),       # 4 chunks
         (2, 64, 1, 128, 32768, BF16, 64),     # 2 chunks, 64 splits for the wide merge
+        # 17..32 heads per K/V head: 1 or 2 head chunks by the same estimate
+        (16, 32, 1, 128, 4096, BF16, 8),      # 2 chunks (1 would merge 32 heads x 16 splits)
+        (4, 32, 1, 128, 16384, BF16, 64),     # 1 chunk: 64 splits for the wide merge
+        (32, 32, 1, 128, 8192, BF16, 8),      # 1 chunk
     ]
     for B, H, G, d, L, dt, S, *grid in cases:
         assert lib.gqa_decode_workspace_size(B, H, G, d, L, dt) == _decode_ws(B, H, S, d, *grid), (B, H, G, d, L, dt, S)
@@ -149,6 +153,7 @@ def test_split_plan_model(lib, monkeypatch):
     assert lib.gqa_decode_workspace_size(64, 64, 8, 128, 32768, BF16) == _decode_ws(64, 64, 8, 128)
     # one split: no workspace
     assert lib.gqa_decode_workspace_size(32, 64, 8, 64, 2048, BF16) == 0
+    assert lib.gqa_decode_workspace_size(128, 32, 1, 128, 1024, BF16) == 0  # 2 head chunks, one split each
 
 
 def test_kernel_selection(lib, monkeypatch):
