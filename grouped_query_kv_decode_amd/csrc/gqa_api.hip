@@ -108,26 +108,63 @@ gqa_status make_plan(int B, int H, int G, int d, int Lmax, gqa_dtype dt, Plan *p
   const int target = env_int("GQA_TARGET_WGS", 256);
   const int max_chunk = env_int("GQA_MAX_CHUNK", 4096);
   const int chunk_env = env_int("GQA_CHUNK", 0);
-  // Split length for a grid of `units` (b, g, head chunk) units.
-  auto chunk_for = [&](long units) {
-    int chunk = chunk_env;
-    if (chunk == 0) {
-      long S = (target + units - 1) / units;
-      if (S < 1) S = 1;
-      chunk = (int)round_up((size_t)ceil_div(Lmax, S), 32);
-      // Floors: the matrix-core kernel's 4 waves take 8 tiles of 32 positions
-      // per 256 (shorter splits cost more in epilogue and merge than they
-      // gain), the VALU kernel's rows are shorter; and at most kMaxSplits
-      // splits per sequence (beyond kMaxFusedSplits merged by a second kernel).
-      const int min_chunk = kind == KIND_MFMA ? 256 : 32;
-      if (chunk < min_chunk) chunk = min_chunk;
-      const int min_for_merge = (int)round_up((size_t)ceil_div(Lmax, kMaxSplits), 32);
-      if (chunk < min_for_merge) chunk = min_for_merge;
-      if (chunk > max_chunk) chunk = max_chunk;
-    }
+  const bool target_env = env_int("GQA_TARGET_WGS", 0) > 0;
+  const int fused_max = env_int("GQA_FUSED_MAX_SPLITS", kMaxFusedSplits);
+  // Split length for about S splits: the floors (the matrix-core kernel's 4
+  // waves take 8 tiles of 32 positions per 256, and shorter splits cost more
+  // in epilogue and merge than they gain; the VALU kernel's rows are
+  // shorter), at most kMaxSplits splits per sequence (beyond kMaxFusedSplits
+  // merged by a second kernel), at most max_chunk positions.
+  auto chunk_of = [&](long S) {
+    int chunk = (int)round_up((size_t)ceil_div(Lmax, S < 1 ? 1 : S), 32);
+    const int min_chunk = kind == KIND_MFMA ? 256 : 32;
+    if (chunk < min_chunk) chunk = min_chunk;
+    const int min_for_merge = (int)round_up((size_t)ceil_div(Lmax, kMaxSplits), 32);
+    if (chunk < min_for_merge) chunk = min_for_merge;
+    if (chunk > max_chunk) chunk = max_chunk;
     return chunk > Lmax ? Lmax : chunk;
   };
-  const int fused_max = env_int("GQA_FUSED_MAX_SPLITS", kMaxFusedSplits);
+  // Split length for a grid of `units` (b, g, head chunk) units of `heads`
+  // query heads each: about `target` workgroups (one per compute unit).  On
+  // the matrix cores the split count is then chosen among the counts that
+  // fill 1..4 rounds of 256 workgroups, by an estimate of the busiest compute
+  // unit's work in KiB: per round one slab (its split's K and V) and ~64 KiB
+  // of fixed cost (first latency, epilogue), plus, when split, the tail of
+  // the split protocol (~128 KiB) and 4x the in-kernel merge (one workgroup
+  // reading heads x splits partials).  Rounding the count up to fill the GPU
+  // leaves a few compute units with two workgroups that set the pace:
+  // B6 H32 G8 d128 L4096 (48 units) 6 splits 26.4 us, 5 splits 21.2 us;
+  // B5 L16384 78.3 -> 56.2 us; B48 L2048 (384 units) 1 split 72.3 us,
+  // 2 splits 64.8 us.  The count stays within the fused merge's limit unless
+  // the length needs more.
+  auto chunk_for = [&](long units, int heads) {
+    if (chunk_env > 0) return chunk_env > Lmax ? Lmax : chunk_env;
+    const int base = chunk_of((target + units - 1) / units);
+    if (kind != KIND_MFMA || target_env) return base;
+    const long s_max = ceil_div(Lmax, base) > fused_max ? ceil_div(Lmax, base) : (long)fused_max;
+    auto est = [&](int chunk) {
+      const long S = ceil_div(Lmax, chunk);
+      const long rounds = (units * S + 255) / 256;
+      double e = rounds * ((double)chunk * d * 4 / 1024 + 64.0);
+      if (S > 1) e += 128.0 + (S > fused_max ? 128.0 : 4.0 * heads * S * (d + 2) * 4 / 1024);
+      return e;
+    };
+    int best = base;
+    double best_e = est(base);
+    for (long k = 1; k <= 4; ++k) {
+      for (long S : {256 * k / units, (256 * k + units - 1) / units}) {
+        if (S < 1) continue;
+        const int c = chunk_of(S);
+        if (ceil_div(Lmax, c) > s_max) continue;
+        const double e = est(c);
+        if (e < best_e) {
+          best_e = e;
+          best = c;
+        }
+      }
+    }
+    return best;
+  };
   if (kind == KIND_MFMA) {
     const int hb = (r + 15) / 16;
     const int hb_all = hb <= 1 ? 1 : (hb <= 2 ? 2 : 4);
@@ -157,11 +194,11 @@ gqa_status make_plan(int B, int H, int G, int d, int Lmax, gqa_dtype dt, Plan *p
       // 28.2 -> 23.2 us; 2 chunks B8 d64 L8192 13.1 us (19.5 with 1)).
       auto cost = [&](int h) {
         const long units = (long)B * G * h;
-        const int chunk = chunk_for(units);
+        const int heads = (hb_all / h) * 16 < r ? (hb_all / h) * 16 : r;
+        const int chunk = chunk_for(units, heads);
         const long S = ceil_div(Lmax, chunk);
         const long rounds = (units * S + 255) / 256;
         const double slab_kib = (double)chunk * d * 4 / 1024 * rounds;
-        const int heads = (hb_all / h) * 16 < r ? (hb_all / h) * 16 : r;
         if (S <= 1) return slab_kib;
         return slab_kib + 128.0 + (S > fused_max ? 128.0 : 4.0 * heads * S * (d + 2) * 4 / 1024);
       };
@@ -180,7 +217,7 @@ gqa_status make_plan(int B, int H, int G, int d, int Lmax, gqa_dtype dt, Plan *p
     pl->HB = 0;
   }
   const long units = (long)B * G * pl->HC;
-  const int chunk = chunk_for(units);
+  const int chunk = chunk_for(units, kind == KIND_MFMA ? (16 * pl->HB < r ? 16 * pl->HB : r) : pl->RC);
   pl->chunk = chunk;
   if (kind == KIND_MFMA) {
     // 4 waves (measured best on every workload with the non-temporal cache

@@ -117,7 +117,8 @@ def _decode_ws(B, H, S, d, grid=0):
 
 
 def test_split_plan_model(lib, monkeypatch):
-    """Split lengths: about 256 workgroups, at least 256 positions on the
+    """Split lengths: about 256 workgroups (on the matrix cores the count
+    that fills whole rounds of 256 best), at least 256 positions on the
     matrix cores (32 on the VALU kernel), at least Lmax/256, at most 4096."""
     for k in ("GQA_CHUNK", "GQA_TARGET_WGS", "GQA_MAX_CHUNK", "GQA_KERNEL", "GQA_HEAD_SPLIT", "GQA_MERGE", "GQA_ORDER",
               "GQA_FUSED_MAX_SPLITS"):
@@ -146,6 +147,13 @@ def test_split_plan_model(lib, monkeypatch):
         (16, 32, 1, 128, 4096, BF16, 8),      # 2 chunks (1 would merge 32 heads x 16 splits)
         (4, 32, 1, 128, 16384, BF16, 64),     # 1 chunk: 64 splits for the wide merge
         (32, 32, 1, 128, 8192, BF16, 8),      # 1 chunk
+        # unit counts that do not divide 256: the split count that fills whole
+        # rounds of 256 workgroups, not the one that just overfills the first
+        (6, 32, 8, 128, 4096, BF16, 5),       # 48 units: 240 workgroups (6 splits: 288)
+        (3, 32, 8, 128, 8192, BF16, 10),      # 24 units: 240 (11 splits: 264)
+        (12, 32, 8, 128, 4096, BF16, 5),      # 96 units: 480, two full rounds (3 splits: 288)
+        (20, 32, 8, 128, 4096, BF16, 3),      # 160 units: 480 (2 splits: 320)
+        (48, 32, 8, 128, 2048, BF16, 2),      # 384 units: 768, three full rounds (1 split: 384)
     ]
     for B, H, G, d, L, dt, S, *grid in cases:
         assert lib.gqa_decode_workspace_size(B, H, G, d, L, dt) == _decode_ws(B, H, S, d, *grid), (B, H, G, d, L, dt, S)
