@@ -335,8 +335,8 @@ def meanpool_bench(args):
 # share of a 64-query-head, 8-K/V-head model split 8 ways, 32/16/128 Gemma-2-
 # like, 64/4/128 a wide group, 16/8/64 - at batch 1 .. 256, contexts 1K .. 128K.
 SERVING_HEADS = [(32, 8, 128), (8, 1, 128), (32, 16, 128), (64, 4, 128), (16, 8, 64)]
-SERVING_BL = [(1, 1024), (1, 32768), (1, 131072), (4, 8192), (16, 1024), (64, 2048), (64, 8192), (256, 1024),
-              (256, 4096)]
+SERVING_BL = [(1, 1024), (1, 32768), (1, 131072), (3, 8192), (4, 8192), (12, 4096), (16, 1024), (20, 4096),
+              (48, 2048), (64, 2048), (64, 8192), (256, 1024), (256, 4096)]
 
 
 def shapes_bench(args):
