@@ -132,7 +132,7 @@ def test_split_plan_model(lib, monkeypatch):
         (64, 64, 8, 128, 32768, BF16, 8, 4096),  # 512 units: 4096 cap; 4096 workgroups, ordered
         (8, 32, 16, 128, 8192, BF16, 2),      # 128 units: 4096
         (1, 8, 2, 64, 256, F32, 8),           # VALU, 2 units: 32-position floor
-        (1, 8, 2, 64, 8192, F32, 128),        # VALU, 2 units: 64-position splits
+        (1, 8, 2, 64, 8192, F32, 256),        # VALU, 2 units of 4 heads: 768 workgroups aimed at, 32-position splits
         (1, 8, 1, 128, 131072, BF16, 256),    # one unit, long: 512-position splits (256 WGs)
         (1, 8, 1, 128, 262144, F32, 256),     # at most 256 splits: 1024 positions
         # 64 heads per K/V head: 2 or 4 head chunks, whichever moves fewer
