@@ -139,12 +139,13 @@ gqa_status make_plan(int B, int H, int G, int d, int Lmax, gqa_dtype dt, Plan *p
   // the length needs more.
   auto chunk_for = [&](long units, int heads) {
     if (chunk_env > 0) return chunk_env > Lmax ? Lmax : chunk_env;
-    // The VALU kernel serving 4 or more heads per row it loads needs several
-    // workgroups per compute unit to hide its dependent FMA chains: 768
-    // (binary32 B16 H32 G8 d128 L4096 214.8 -> 101.5 us, B12 L2048 80.4 ->
-    // 44.0 us); with 1 or 2 heads one per compute unit stays best (B8 H32
-    // G16 d128 L8192: 154.3 us, 166.0 with 768).
-    const long tgt = (kind == KIND_VALU && heads >= 4 && !target_env) ? 768 : target;
+    // The VALU kernel on binary32 serving 4 or more heads per row it loads
+    // needs several workgroups per compute unit to hide its dependent FMA
+    // chains: 768 (B16 H32 G8 d128 L4096 214.8 -> 101.5 us, B12 L2048
+    // 80.4 -> 44.0 us); with 1 or 2 heads one per compute unit stays best
+    // (B8 H32 G16 d128 L8192: 154.3 us, 166.0 with 768), and on bfloat16
+    // (only run there when forced) 768 is slower on the T5-XXL shapes.
+    const long tgt = (kind == KIND_VALU && dt == GQA_F32 && heads >= 4 && !target_env) ? 768 : target;
     const int base = chunk_of((tgt + units - 1) / units);
     if (kind != KIND_MFMA || target_env) return base;
     const long s_max = ceil_div(Lmax, base) > fused_max ? ceil_div(Lmax, base) : (long)fused_max;
