@@ -252,6 +252,32 @@ def test_dispatch_order_large_batch(env, dtype):
     check(ref[rows], oracle_out(q, k, v, lt, scale, rows=rows), dtype, "B5000 ordered, sampled rows")
 
 
+PLAN_SHAPES = [
+    # (B, H, G, d, L, dtype): default plans chosen by the launch estimates
+    (6, 32, 8, 128, 4096, "bf16"),     # 48 units: 5 splits, 240 workgroups
+    (12, 32, 8, 128, 4096, "bf16"),    # 96 units: 5 splits, two full rounds
+    (48, 32, 8, 128, 2048, "bf16"),    # 384 units: 2 splits, three full rounds
+    (4, 32, 1, 128, 16384, "bf16"),    # 32 heads per K/V head: 1 head chunk, 64 splits (wide merge)
+    (64, 64, 1, 64, 4096, "bf16"),     # 64 heads per K/V head: 2 head chunks
+    (12, 32, 8, 128, 2048, "f32"),     # binary32, VALU kernel aiming at 768 workgroups
+]
+
+
+@pytest.mark.parametrize("shape", PLAN_SHAPES, ids=lambda c: "B%d_H%d_G%d_d%d_L%d_%s" % c)
+def test_default_plan_shapes(env, shape):
+    """Shapes whose default plans come from the split-count, head-chunk and
+    binary32 target estimates, against the oracle on sampled sequences
+    (ragged lengths keep every split path busy)."""
+    B, H, G, d, L, dtype = shape
+    gen = torch.Generator().manual_seed(B * 131 + L)
+    lens = [int(x) for x in torch.randint(1, L + 1, (B,), generator=gen)]
+    lens[0] = L
+    q, k, v, lt, scale = rand_case(B, H, G, d, L, lens, dtype, seed=90 + B)
+    out = run_gpu(q, k, v, lt, scale)
+    rows = sorted(set([0, 1, B // 2, B - 1]))
+    check(out[rows], oracle_out(q, k, v, lt, scale, rows=rows), dtype, "plan shape %s" % (shape,))
+
+
 def test_very_long_sequence(env):
     """2,097,152 positions: the 4096-position split cap gives 512 splits (more
     than the planner's usual 256), merged by the wide kernel 16 per slice."""
