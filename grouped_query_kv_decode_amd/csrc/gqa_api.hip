@@ -77,16 +77,19 @@ gqa_status check_shape(int B, int H, int G, int d, int Lmax, gqa_dtype dt) {
 //  - workgroups of the matrix-core kernel have 4 waves (GQA_WAVES = 8 or 16
 //    overrides where the register budget for the head blocks allows).
 //  - with fewer (b, g) units than compute units the matrix-core kernel
-//    spreads a group's head blocks over 2 or 4 workgroups (GQA_HEAD_SPLIT),
-//    which then load the cache with plain instead of non-temporal loads
-//    (GQA_TEMPORAL=0/1 overrides) so that they share its lines in L2.
-//  - splits: one workgroup per (b, g, head chunk, split).  The split length
-//    is chosen so that the grid holds about GQA_TARGET_WGS = 256 workgroups
-//    (one per compute unit), at least 256 positions (matrix cores) or 32
-//    (VALU), at least Lmax/256, at most GQA_MAX_CHUNK = 4096: long splits
-//    amortise each workgroup's prologue and epilogue, the cap keeps ragged
-//    batches balanced.  Half the compute units cannot keep HBM busy, so a
-//    shape with fewer (b, g) units than that is split.
+//    spreads a group's head blocks over up to 2 or 4 workgroups (head chunks;
+//    how many by an estimate of the busiest compute unit's work, see
+//    plan_cost; GQA_HEAD_SPLIT overrides), which then load the cache with
+//    plain instead of non-temporal loads (GQA_TEMPORAL=0/1 overrides) so
+//    that they share its lines in L2.
+//  - splits: one workgroup per (b, g, head chunk, split), split lengths of
+//    at least 256 positions (matrix cores) or 32 (VALU), at least Lmax/256,
+//    at most GQA_MAX_CHUNK = 4096 (the cap keeps ragged batches balanced).
+//    The VALU kernel aims at one workgroup per compute unit (three on
+//    binary32 with 4 or more heads per row set); the matrix-core kernel takes
+//    the split count of lowest plan_cost among those filling 1..4 rounds of
+//    256 workgroups.  GQA_TARGET_WGS (a plain workgroup target) and
+//    GQA_CHUNK override.
 //  - when a sequence spans several splits, the workgroup that finishes its
 //    (b, g) unit last merges the partials inside the same kernel; with more
 //    units than counters (or GQA_MERGE=kernel) a second kernel merges instead.
@@ -124,19 +127,30 @@ gqa_status make_plan(int B, int H, int G, int d, int Lmax, gqa_dtype dt, Plan *p
     if (chunk > max_chunk) chunk = max_chunk;
     return chunk > Lmax ? Lmax : chunk;
   };
+  // Estimated time of a matrix-core launch, in KiB through the busiest
+  // compute unit (its memory path moves ~35 GB/s, from L2 or HBM alike):
+  // per dispatch round one slab (a split's K and V, bfloat16) plus ~64 KiB of
+  // fixed cost (first latency, epilogue); when the sequence is split, ~128
+  // KiB for the split protocol's tail (partial stores, arrival) plus the
+  // merge - the in-kernel one is a single workgroup reading heads x splits
+  // partials at the very end (x4), the wide merge kernel a launch of its own
+  // (~128 KiB).
+  auto plan_cost = [&](long units, int heads, int chunk) {
+    const long S = ceil_div(Lmax, chunk);
+    const long rounds = (units * S + 255) / 256;
+    double e = rounds * ((double)chunk * d * 4 / 1024 + 64.0);
+    if (S > 1) e += 128.0 + (S > fused_max ? 128.0 : 4.0 * heads * S * (d + 2) * 4 / 1024);
+    return e;
+  };
   // Split length for a grid of `units` (b, g, head chunk) units of `heads`
   // query heads each: about `target` workgroups (one per compute unit).  On
-  // the matrix cores the split count is then chosen among the counts that
-  // fill 1..4 rounds of 256 workgroups, by an estimate of the busiest compute
-  // unit's work in KiB: per round one slab (its split's K and V) and ~64 KiB
-  // of fixed cost (first latency, epilogue), plus, when split, the tail of
-  // the split protocol (~128 KiB) and 4x the in-kernel merge (one workgroup
-  // reading heads x splits partials).  Rounding the count up to fill the GPU
-  // leaves a few compute units with two workgroups that set the pace:
-  // B6 H32 G8 d128 L4096 (48 units) 6 splits 26.4 us, 5 splits 21.2 us;
-  // B5 L16384 78.3 -> 56.2 us; B48 L2048 (384 units) 1 split 72.3 us,
-  // 2 splits 64.8 us.  The count stays within the fused merge's limit unless
-  // the length needs more.
+  // the matrix cores the split count is then the one of lowest plan_cost
+  // among the counts that fill 1..4 rounds of 256 workgroups.  Rounding the
+  // count up to fill the GPU leaves a few compute units with two workgroups
+  // that set the pace: B6 H32 G8 d128 L4096 (48 units) 6 splits 26.4 us,
+  // 5 splits 21.2 us; B5 L16384 78.3 -> 56.2 us; B48 L2048 (384 units)
+  // 1 split 72.3 us, 2 splits 64.8 us.  The count stays within the fused
+  // merge's limit unless the length needs more.
   auto chunk_for = [&](long units, int heads) {
     if (chunk_env > 0) return chunk_env > Lmax ? Lmax : chunk_env;
     // The VALU kernel on binary32 serving 4 or more heads per row it loads
@@ -149,13 +163,7 @@ gqa_status make_plan(int B, int H, int G, int d, int Lmax, gqa_dtype dt, Plan *p
     const int base = chunk_of((tgt + units - 1) / units);
     if (kind != KIND_MFMA || target_env) return base;
     const long s_max = ceil_div(Lmax, base) > fused_max ? ceil_div(Lmax, base) : (long)fused_max;
-    auto est = [&](int chunk) {
-      const long S = ceil_div(Lmax, chunk);
-      const long rounds = (units * S + 255) / 256;
-      double e = rounds * ((double)chunk * d * 4 / 1024 + 64.0);
-      if (S > 1) e += 128.0 + (S > fused_max ? 128.0 : 4.0 * heads * S * (d + 2) * 4 / 1024);
-      return e;
-    };
+    auto est = [&](int chunk) { return plan_cost(units, heads, chunk); };
     int best = base;
     double best_e = est(base);
     for (long k = 1; k <= 4; ++k) {
@@ -185,29 +193,19 @@ gqa_status make_plan(int B, int H, int G, int d, int Lmax, gqa_dtype dt, Plan *p
     };
     hc = fit(hc);
     if (hc > 1) {
-      // Every head chunk reads the whole slab, through a compute unit's
-      // memory path (~35 GB/s, from L2 or HBM alike), and the in-kernel merge
-      // is one workgroup reading heads x splits partials.  Fewer chunks read
-      // less; more chunks keep the splits, and so the merge, small.  Estimate
-      // both candidates (1 or 2 chunks for two head blocks, 2 or 4 for four)
-      // in KiB through the slowest compute unit: its workgroups' slabs, plus,
-      // when the sequence is split, the tail of the split protocol (partial
-      // stores, arrival, merge: ~128 KiB worth) and the fused merge (serial,
-      // at the end: x4) or the wide merge kernel's launch (~128 KiB worth).
-      // Picks the faster plan on 21 of 22 measured shapes (bf16; 64 heads per
-      // K/V head: 2 chunks B64 d64 L4096 29.0 -> 23.2 us, B2 d128 L32768
-      // 32.9 -> 22.8 us; 4 chunks B4 d64 L8192 12.8 us (19.6 with 2); 32
-      // heads: 1 chunk B4 d128 L16384 25.1 -> 19.0 us, B1 d128 L131072
-      // 28.2 -> 23.2 us; 2 chunks B8 d64 L8192 13.1 us (19.5 with 1)).
+      // Every head chunk reads the whole slab through a compute unit's memory
+      // path; fewer chunks read less, more chunks keep the splits, and so the
+      // merge, small.  Of the two candidates (1 or 2 chunks for two head
+      // blocks, 2 or 4 for four) the one of lower plan_cost wins.  Measured
+      // (bf16): 64 heads per K/V head, 2 chunks B64 d64 L4096 29.0 -> 23.2
+      // us, B2 d128 L32768 32.9 -> 22.8 us, 4 chunks B4 d64 L8192 12.8 us
+      // (19.6 with 2); 32 heads, 1 chunk B4 d128 L16384 25.1 -> 19.0 us,
+      // B1 d128 L131072 28.2 -> 23.2 us, 2 chunks B8 d64 L8192 13.1 us
+      // (19.5 with 1).
       auto cost = [&](int h) {
         const long units = (long)B * G * h;
         const int heads = (hb_all / h) * 16 < r ? (hb_all / h) * 16 : r;
-        const int chunk = chunk_for(units, heads);
-        const long S = ceil_div(Lmax, chunk);
-        const long rounds = (units * S + 255) / 256;
-        const double slab_kib = (double)chunk * d * 4 / 1024 * rounds;
-        if (S <= 1) return slab_kib;
-        return slab_kib + 128.0 + (S > fused_max ? 128.0 : 4.0 * heads * S * (d + 2) * 4 / 1024);
+        return plan_cost(units, heads, chunk_for(units, heads));
       };
       const int other = fit(hc / 2);  // at most two head blocks per workgroup (four measured slower)
       if (other != hc && hb_all / other <= 2 && cost(other) < cost(hc)) hc = other;
@@ -243,7 +241,7 @@ gqa_status make_plan(int B, int H, int G, int d, int Lmax, gqa_dtype dt, Plan *p
   // In-kernel merge: one counter per unit, and a merging workgroup that
   // reads every split of its heads, which pays up to kMaxFusedSplits; beyond
   // that a merge kernel spread over heads, dimensions and splits.
-  pl->wide = pl->S > env_int("GQA_FUSED_MAX_SPLITS", kMaxFusedSplits);
+  pl->wide = pl->S > fused_max;
   pl->fused = units <= kMaxFusedUnits && !pl->wide && !(merge && strcmp(merge, "kernel") == 0);
   // Grids of several rounds with at least kOrderMinSplits splits per
   // sequence: the order kernel sorts the items largest first (ragged lengths
