@@ -147,6 +147,7 @@ def test_split_plan_model(lib, monkeypatch):
         (16, 32, 1, 128, 4096, BF16, 8),      # 2 chunks (1 would merge 32 heads x 16 splits)
         (4, 32, 1, 128, 16384, BF16, 64),     # 1 chunk: 64 splits for the wide merge
         (32, 32, 1, 128, 8192, BF16, 8),      # 1 chunk
+        (96, 32, 1, 128, 2048, BF16, 2),      # 1 chunk, 2 splits: 192 workgroups in one round
         # unit counts that do not divide 256: the split count that fills whole
         # rounds of 256 workgroups, not the one that just overfills the first
         (6, 32, 8, 128, 4096, BF16, 5),       # 48 units: 240 workgroups (6 splits: 288)
