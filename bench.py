@@ -19,6 +19,8 @@ Other modes (used to produce the files under profiles/):
     --meanpool                 the mean-pool conversion step (one JSON line)
     --calibrate-copy           plain device copy of a known size, for scaling
                                the FETCH_SIZE / WRITE_SIZE counters
+    --read-ceiling             the streaming-read probe: what a kernel that only
+                               reads (16-byte loads) gets from HBM
     --summarize-rocprof DIR    print a summary of rocprofv3 CSV output
 """
 from __future__ import annotations
@@ -286,6 +288,40 @@ def fig6(args):
         torch.cuda.empty_cache()
 
 
+def read_ceiling(args):
+    """The practical HBM read ceiling: gqa_stream_read over 1 GiB buffers (4,
+    rotated: beyond the 256 MB Infinity Cache), plain and non-temporal 16-byte
+    loads, several grid sizes.  One JSON line per setting, then the best."""
+    import torch
+    import grouped_query_kv_decode_amd as gqa
+    dev = torch.device("cuda:0")
+    gqa.load_library()
+    n = 1 << 30
+    bufs = [torch.empty(n, dtype=torch.uint8, device=dev).fill_(i + 1) for i in range(4)]
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    best = None
+    for nt in (False, True):
+        for grid in (1024, 2048, 4096, 8192):
+            for i in range(3):
+                gqa.stream_read(bufs[i % 4], nt, grid, sink)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            iters = 40
+            e0.record(stream)
+            for i in range(iters):
+                gqa.stream_read(bufs[i % 4], nt, grid, sink)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / iters
+            line = {"mode": "read_ceiling", "nontemporal": nt, "grid": grid, "bytes": n, "us_per_call": us,
+                    "GBps": n / us / 1e3, "frac_of_8TBps": n / us / 8e6}
+            print(json.dumps(line), flush=True)
+            if best is None or line["GBps"] > best["GBps"]:
+                best = line
+    print(json.dumps(dict(best, mode="read_ceiling_best")), flush=True)
+
+
 def calibrate_copy(args):
     """A plain device-to-device copy of a known size (for counter scaling)."""
     import torch
@@ -455,6 +491,7 @@ def main():
     ap.add_argument("--window", type=int, default=4096, help="window for --variant window/append (0: none)")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time to aim for")
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--read-ceiling", action="store_true", help="the streaming-read probe (read ceiling of HBM)")
     ap.add_argument("--meanpool", action="store_true", help="time the K/V mean-pool conversion step")
     ap.add_argument("--fig6", action="store_true", help="the pages' fig. 6 group sweep as decoder attention")
     ap.add_argument("--fig6-batch", type=int, default=32)
@@ -483,6 +520,9 @@ def main():
         return 0
     if args.calibrate_copy:
         calibrate_copy(args)
+        return 0
+    if args.read_ceiling:
+        read_ceiling(args)
         return 0
     if args.fig6:
         fig6(args)

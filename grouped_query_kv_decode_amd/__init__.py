@@ -18,6 +18,7 @@ Entry points (same names as the C ABI, without the ``gqa_`` prefix):
     decode_layer(x, w_qkv, w_o, k_cache, v_cache, seq_lens, H, G, scale, window=0)
     meanpool_kv(w, H, G, out=None)
     decode_kernel_kind(B, H, G, d, Lmax, dtype)
+    stream_read(buf, nontemporal=True, grid=0, sink=None)   the read-ceiling probe (measurement only)
 """
 from __future__ import annotations
 
@@ -27,7 +28,7 @@ import os
 __all__ = [
     "GQAError", "decode", "decode_phase", "decode_window", "decode_append", "decode_workspace_size", "workspace_init", "meanpool_kv",
     "linear", "linear_workspace_size", "pack_weight", "linear_packed", "decode_layer", "decode_layer_workspace_size", "LayerStep",
-    "decode_kernel_kind", "status_string", "library_path", "load_library", "Decoder",
+    "decode_kernel_kind", "stream_read", "status_string", "library_path", "load_library", "Decoder",
     "GQA_F32", "GQA_BF16",
 ]
 
@@ -44,7 +45,7 @@ EXPORTED = [
     "gqa_decode_append", "gqa_linear_workspace_size", "gqa_linear", "gqa_pack_weight", "gqa_linear_packed",
     "gqa_decode_layer_workspace_size",
     "gqa_decode_layer", "gqa_meanpool_kv",
-    "gqa_status_string", "gqa_last_hip_error", "gqa_decode_kernel_kind",
+    "gqa_status_string", "gqa_last_hip_error", "gqa_decode_kernel_kind", "gqa_stream_read",
 ]
 
 _lib = None
@@ -107,6 +108,8 @@ def load_library(path: str | None = None):
     lib.gqa_last_hip_error.argtypes = []
     lib.gqa_decode_kernel_kind.restype = ci
     lib.gqa_decode_kernel_kind.argtypes = [ci, ci, ci, ci, ci, ci]
+    lib.gqa_stream_read.restype = ci
+    lib.gqa_stream_read.argtypes = [vp, sz, ci, ci, vp, vp]
     if path is None:
         _lib = lib
     return lib
@@ -433,3 +436,20 @@ def meanpool_kv(w, H: int, G: int, out=None):
     if st:
         raise GQAError(st, "gqa_meanpool_kv")
     return out
+
+
+def stream_read(buf, nontemporal: bool = True, grid: int = 0, sink=None):
+    """Read every byte of the GPU tensor `buf` once (16-byte loads,
+    non-temporal by default) on `grid` workgroups (0: 2048): the read-ceiling
+    probe.  Returns `sink` (one int32 on the GPU), written only when a
+    thread's xor fold of its pieces equals 0x12345678."""
+    import torch
+    if buf.device.type != "cuda" or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous tensor on the GPU")
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device=buf.device)
+    st = load_library().gqa_stream_read(buf.data_ptr(), buf.numel() * buf.element_size(), int(bool(nontemporal)),
+                                        int(grid), sink.data_ptr(), _stream_handle(buf.device))
+    if st:
+        raise GQAError(st, "gqa_stream_read")
+    return sink

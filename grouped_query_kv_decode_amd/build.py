@@ -37,6 +37,7 @@ SOURCES = [
     ("gqa_decode_valu.hip", []),
     ("gqa_merge.hip", []),
     ("gqa_order.hip", []),
+    ("gqa_stream.hip", []),
     ("gqa_linear.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]),
     ("gqa_linear_packed.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]),
     # bit-exact conversion arithmetic: no contraction of any kind

@@ -675,6 +675,17 @@ const char *gqa_status_string(gqa_status s) {
   return "unknown status";
 }
 
+gqa_status gqa_stream_read(const void *buf, size_t bytes, int nontemporal, int grid, unsigned *sink,
+                           hipStream_t stream) {
+  if (grid < 0 || grid > 1 << 20) return GQA_ERR_SHAPE;
+  if (bytes == 0) return GQA_OK;
+  if (!buf || !sink) return GQA_ERR_NULL;
+  if (!aligned(buf, 16) || bytes % 16 != 0) return GQA_ERR_ALIGN;
+  const hipError_t e = gqa::launch_stream_read(buf, bytes, nontemporal != 0, grid == 0 ? 2048u : (unsigned)grid, sink,
+                                               stream);
+  return e == hipSuccess ? GQA_OK : hip_fail(e);
+}
+
 const char *gqa_last_hip_error(void) { return g_last_hip_error.c_str(); }
 
 }  // extern "C"

@@ -203,5 +203,7 @@ hipError_t launch_merge_wide(const DecodeParams &p, int dtype, int D, hipStream_
 hipError_t launch_order(const DecodeParams &p, bool valu_layout, unsigned grid, int *order, hipStream_t stream);
 hipError_t launch_meanpool(const float *w, int d_model, int H, int G, int h, float *w_out, hipStream_t stream);
 hipError_t launch_fill_zero(void *ptr, size_t bytes, hipStream_t stream);
+hipError_t launch_stream_read(const void *buf, size_t bytes, bool nontemporal, unsigned grid, unsigned *sink,
+                              hipStream_t stream);
 
 }  // namespace gqa

@@ -266,6 +266,22 @@ gqa_status gqa_decode_layer(const void *x, const void *w_qkv_packed, const void 
  */
 gqa_status gqa_meanpool_kv(const float *w, int d_model, int H, int G, int h, float *w_out, hipStream_t stream);
 
+/*
+ * Measurement utility (not part of the decode path): reads `bytes` of `buf`
+ * once with 16-byte loads, non-temporal if `nontemporal` is nonzero - the
+ * loads of the decode kernels' cache stream - on `grid` workgroups of 256
+ * threads (0: 2048), each thread taking pieces grid-stride.  The practical
+ * read ceiling of the GPU, against which the decode kernels' rates are put.
+ * Every thread folds its pieces with xor and writes the fold to sink[0] only
+ * if it equals 0x12345678, so no read can be skipped and sink is normally
+ * left untouched.
+ *   buf   device, 16-byte aligned; bytes a multiple of 16 (GQA_ERR_ALIGN).
+ *   sink  device, one unsigned; grid in 0..2^20 (GQA_ERR_SHAPE otherwise).
+ * bytes = 0 is a no-op.  Enqueued on `stream`.
+ */
+gqa_status gqa_stream_read(const void *buf, size_t bytes, int nontemporal, int grid, unsigned *sink,
+                           hipStream_t stream);
+
 /* Static description of a status code. */
 const char *gqa_status_string(gqa_status status);
 

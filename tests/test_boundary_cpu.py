@@ -195,6 +195,18 @@ def test_workspace_init_arguments(lib):
     assert lib.gqa_workspace_init(None, 64, None) == NULL
 
 
+def test_stream_read_arguments(lib):
+    """The read-ceiling probe's host checks (nothing is launched)."""
+    sr = lib.gqa_stream_read
+    assert sr(P, 0, 1, 0, P, None) == OK          # no bytes: no-op
+    assert sr(None, 64, 1, 0, P, None) == NULL
+    assert sr(P, 64, 1, 0, None, None) == NULL
+    assert sr(P + 8, 64, 1, 0, P, None) == ALIGN  # buffer not 16-byte aligned
+    assert sr(P, 72, 1, 0, P, None) == ALIGN      # size not a multiple of 16
+    assert sr(P, 64, 1, -1, P, None) == SHAPE
+    assert sr(P, 64, 1, (1 << 20) + 1, P, None) == SHAPE
+
+
 def test_phase_argument(lib):
     args = (P, P, P, P, 2, 8, 2, 128, 512, 0.125, BF16, P, P, 1 << 30, None)
     assert lib.gqa_decode_phase(3, *args) == UNSUP
