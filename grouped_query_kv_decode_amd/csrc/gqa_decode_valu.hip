@@ -51,7 +51,7 @@ __device__ __forceinline__ float row_sum(float x) {
   return x;
 }
 
-template <typename T, int D, int RC, int U>
+template <typename T, int D, int RC, int U, bool SPEC>
 __global__ __launch_bounds__(256) void decode_valu(DecodeParams p) {
   constexpr int EPL = Elems<T>::kPerLane;  // elements per lane per row
   constexpr int LPR = D / EPL;             // lanes per row
@@ -73,13 +73,54 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeParams p) {
   const int g = id % p.G;
   const int b = id / p.G;
 
+  const int jbase = hc * RC;
+  const int nh = min(RC, p.r - jbase);
+  const int head0 = g * p.r + jbase;
+  const bool append = p.k_new != nullptr;
+  const size_t slab = ((size_t)b * p.G + g) * (size_t)p.Lmax * D;
+  const T *kp = static_cast<const T *>(p.k) + slab + sub * EPL;
+  const T *vp = static_cast<const T *>(p.v) + slab + sub * EPL;
+
+  // Query rows of the served heads (they do not depend on the length).
+  uint4 qraw[RC];
+#pragma unroll
+  for (int j = 0; j < RC; ++j)
+    qraw[j] = j < nh ? *reinterpret_cast<const uint4 *>(static_cast<const T *>(p.q) +
+                                                       ((size_t)b * p.H + head0 + j) * D + sub * EPL)
+                     : make_uint4(0u, 0u, 0u, 0u);
+
+  // A slot of rows: U rows per row group, their validity in the split.
+  struct Rows {
+    uint4 kr[U], vr[U];
+    bool ok[U];
+  };
+  constexpr int kStep = NRG * U;
+  // SPEC (grids of one round, no cache append): the first slot is
+  // requested before the sequence length arrives (as in the matrix-core
+  // kernel), for a full-length sequence, rows clamped inside the slab.  Once
+  // the length is known, the slot is used if the split starts where
+  // guessed: rows past the split are masked and their V set to zero
+  // (padding may hold anything), so the products equal those of the plain
+  // path.  Only on the leading splits.  Tiny binary32 B1 H8 G2 d64 L256:
+  // 9.1 -> 8.5 us; on larger grids the variant's code streamed slower
+  // (binary32 Mistral-7B shape 93 -> 109 us), so they run without it.
+  const int lo_guess = p.window > 0 && p.Lmax > p.window ? p.Lmax - p.window : 0;
+  const int ts_guess = lo_guess + s * p.chunk;
+  const bool spec = SPEC && (s == 0 || p.S <= 2) && ts_guess < p.Lmax;
+  Rows first;
+  if (spec) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int row = min(ts_guess + u * NRG + rg, p.Lmax - 1);
+      first.kr[u] = stream_load(reinterpret_cast<const uint4 *>(kp + (size_t)row * D));
+      first.vr[u] = stream_load(reinterpret_cast<const uint4 *>(vp + (size_t)row * D));
+    }
+  }
+
   const int n = clamp_len(p, b);
   const int lo = window_lo(p, n);
   const int nsplit = num_splits(n - lo, p.chunk);
   if (s >= nsplit) return;
-  const int jbase = hc * RC;
-  const int nh = min(RC, p.r - jbase);
-  const int head0 = g * p.r + jbase;
   if (n == 0) {
     write_zero_heads<T, D>(p, b, head0, nh);
     return;
@@ -87,28 +128,18 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeParams p) {
   const int t0 = lo + s * p.chunk, t1 = min(t0 + p.chunk, n);
   // Cache append: position n-1 is read from k_new / v_new and written into
   // the cache by one workgroup of the last split.
-  const bool append = p.k_new != nullptr;
   if (append && s == nsplit - 1 && hc == 0) append_row<T, D>(p, b, g, n);
+  const bool use_first = spec && t0 == ts_guess;
 
-  // Query rows of the served heads, pre-multiplied by scale*log2(e).
+  // Query rows pre-multiplied by scale*log2(e) (zero rows past the group).
   float qf[RC][EPL];
 #pragma unroll
   for (int j = 0; j < RC; ++j) {
-    if (j < nh) {
-      const uint4 u = *reinterpret_cast<const uint4 *>(static_cast<const T *>(p.q) +
-                                                      ((size_t)b * p.H + head0 + j) * D + sub * EPL);
-      Elems<T>::widen(u, qf[j]);
+    Elems<T>::widen(qraw[j], qf[j]);
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) qf[j][e] *= p.scale_log2;
-    } else {
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) qf[j][e] = 0.f;
-    }
+    for (int e = 0; e < EPL; ++e) qf[j][e] *= p.scale_log2;
   }
 
-  const size_t slab = ((size_t)b * p.G + g) * (size_t)p.Lmax * D;
-  const T *kp = static_cast<const T *>(p.k) + slab + sub * EPL;
-  const T *vp = static_cast<const T *>(p.v) + slab + sub * EPL;
   const T *knew = append ? static_cast<const T *>(p.k_new) + ((size_t)b * p.G + g) * D + sub * EPL : nullptr;
   const T *vnew = append ? static_cast<const T *>(p.v_new) + ((size_t)b * p.G + g) * D + sub * EPL : nullptr;
 
@@ -121,10 +152,6 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeParams p) {
     for (int e = 0; e < EPL; ++e) o[j][e] = 0.f;
   }
 
-  struct Rows {
-    uint4 kr[U], vr[U];
-    bool ok[U];
-  };
   auto load = [&](Rows &R, int tb) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -134,6 +161,14 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeParams p) {
       const bool fresh = append && row == n - 1;
       R.kr[u] = stream_load(reinterpret_cast<const uint4 *>(fresh ? knew : kp + (size_t)row * D));
       R.vr[u] = stream_load(reinterpret_cast<const uint4 *>(fresh ? vnew : vp + (size_t)row * D));
+    }
+  };
+  // The speculative slot once the split is known: rows past it masked, with V zero.
+  auto settle = [&](Rows &R, int tb) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      R.ok[u] = tb + u * NRG + rg < t1;
+      if (!R.ok[u]) R.vr[u] = make_uint4(0u, 0u, 0u, 0u);
     }
   };
   auto process = [&](const Rows &R) {
@@ -189,12 +224,15 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeParams p) {
   // the tiny B1 H8 G2 d64 L256 case 8.8 -> 8.0 us.  With 1, 2 or 8 heads
   // the slots' registers cost occupancy (2 heads, B8 H32 G16 d128 L8192:
   // 156.5 -> 209.5 us), so those load and multiply one slot at a time.
-  constexpr int kStep = NRG * U;
   constexpr bool kRing = RC == 4;
   if constexpr (kRing) {
     const int nit = (t1 - t0 + kStep - 1) / kStep;
-    Rows A, B;
-    load(A, t0);
+    Rows &A = first;
+    Rows B;
+    if (use_first)
+      settle(A, t0);
+    else
+      load(A, t0);
     int i = 0;
     for (; i + 2 < nit; i += 2) {
       load(B, t0 + (i + 1) * kStep);
@@ -210,7 +248,13 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeParams p) {
       process(A);
     }
   } else {
-    for (int tb = t0; tb < t1; tb += kStep) {
+    int tb = t0;
+    if (use_first) {
+      settle(first, t0);
+      process(first);
+      tb += kStep;
+    }
+    for (; tb < t1; tb += kStep) {
       Rows R;
       load(R, tb);
       process(R);
@@ -290,7 +334,10 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeParams p) {
 template <typename T, int D, int RC>
 hipError_t launch_t(const DecodeParams &p, unsigned grid, hipStream_t stream) {
   constexpr int U = RC <= 4 ? 8 : 4;
-  hipLaunchKernelGGL((decode_valu<T, D, RC, U>), dim3(grid), dim3(256), 0, stream, p);
+  if (grid <= 256 && p.k_new == nullptr)
+    hipLaunchKernelGGL((decode_valu<T, D, RC, U, true>), dim3(grid), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((decode_valu<T, D, RC, U, false>), dim3(grid), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
