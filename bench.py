@@ -147,6 +147,12 @@ def run_bench(args):
     kv_bytes = 2 * w.B * w.G * w.Lmax * w.d * (4 if w.dtype == "f32" else 2)
     rot = args.rotate if args.rotate else max(1, math.ceil((1 << 30) / kv_bytes))
     window = args.window if args.variant in ("window", "append") else 0
+    # --graph: the calls are bound to a side stream and the K timed steps are
+    # captured there into one HIP graph, replayed once in the timed region
+    # (what a serving loop replaying graphs sees: no host launch cost).
+    side = torch.cuda.Stream(dev) if args.graph else None
+    if side is not None:
+        torch.cuda.set_stream(side)
     sets, decs = [], []
     for i in range(rot):
         q, k, v, lens = wl.make_inputs(w, dev, pad="none", seed_offset=i)
@@ -178,12 +184,23 @@ def run_bench(args):
     # is the kernel's average duration including the back-to-back launch gaps.
     K = args.steps
     stream = torch.cuda.current_stream()
+    graph = None
+    if side is not None:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            for i in range(K):
+                decs[i % rot]()
+        graph.replay()
+        torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record(stream)
-    for i in range(K):
-        decs[i % rot]()
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(K):
+            decs[i % rot]()
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -218,6 +235,7 @@ def run_bench(args):
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic},
         "alg_bytes_per_step": ab,
         "kernel_us_avg": avg_kernel_ms * 1e3,
+        "timing": "hip_graph" if graph is not None else "eager",
         "kernels_per_step": kernels_per_step,
         "hbm_gbps_wall": ab / (ms_per_step * 1e-3) / 1e9,
     }
@@ -320,6 +338,36 @@ def read_ceiling(args):
             if best is None or line["GBps"] > best["GBps"]:
                 best = line
     print(json.dumps(dict(best, mode="read_ceiling_best")), flush=True)
+    # The floor of a call: the same kernel reading one 16-byte piece, on 1 and
+    # on 256 workgroups, 400 calls back to back from this Python loop (bound
+    # by the host's cost per call) and as one replay of a HIP graph of the
+    # 400 calls (the GPU's own cost per launch).
+    tiny = bufs[0][:16]
+    iters = 400
+    for grid in (1, 256):
+        for i in range(20):
+            gqa.stream_read(tiny, True, grid, sink)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(iters):
+            gqa.stream_read(tiny, True, grid, sink)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        eager = e0.elapsed_time(e1) * 1e3 / iters
+        side = torch.cuda.Stream(dev)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            for i in range(iters):
+                gqa.stream_read(tiny, True, grid, sink)
+        g.replay()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": "launch_floor", "grid": grid, "bytes": 16, "us_per_call": eager,
+                          "us_per_call_graph": e0.elapsed_time(e1) * 1e3 / iters}), flush=True)
 
 
 def calibrate_copy(args):
@@ -485,6 +533,8 @@ def main():
     ap.add_argument("--workload", default="mistral7b_bf16_B16_H32_G8_d128_L4096")
     ap.add_argument("--rotate", type=int, default=0, help="input sets cycled through (default: >= 1 GiB of caches)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="time one replay of the K steps captured into a HIP graph (no host launch cost)")
     ap.add_argument("--variant", choices=["decode", "append", "window", "layer"], default="decode",
                     help="decode (default), decode with the cache append, sliding-window decode, or the whole "
                          "decode step of a layer (q/k/v projection, append + attention, output projection)")
