@@ -84,7 +84,8 @@ gqa_status check_shape(int B, int H, int G, int d, int Lmax, gqa_dtype dt) {
 //    that they share its lines in L2.
 //  - splits: one workgroup per (b, g, head chunk, split), split lengths of
 //    at least 256 positions (matrix cores) or 32 (VALU), at least Lmax/256,
-//    at most GQA_MAX_CHUNK = 4096 (the cap keeps ragged batches balanced).
+//    at most GQA_MAX_CHUNK = 8192 on the matrix cores, 4096 on the VALU
+//    kernel (the cap keeps ragged batches balanced).
 //    The VALU kernel aims at one workgroup per compute unit (three on
 //    binary32 with 4 or more heads per row set); the matrix-core kernel takes
 //    the split count of lowest plan_cost among those filling 1..4 rounds of
@@ -109,7 +110,11 @@ gqa_status make_plan(int B, int H, int G, int d, int Lmax, gqa_dtype dt, Plan *p
   pl->kind = kind;
   pl->NW = 4;
   const int target = env_int("GQA_TARGET_WGS", 256);
-  const int max_chunk = env_int("GQA_MAX_CHUNK", 4096);
+  // Split cap: 8192 positions on the matrix cores, measured against 4096 and
+  // 6144 (ragged B64 H64 G8 d128 Lmax 32768 715 -> 707 us, B64 H64 G8 L16384
+  // 664 -> 652 us, B32 H64 G8 L8192 164.5 -> 159 us, B8 H32 G8 L131072
+  // 652 -> 641 us, no shape slower; 6144 leaves odd round counts).
+  const int max_chunk = env_int("GQA_MAX_CHUNK", kind == KIND_MFMA ? 8192 : 4096);
   const int chunk_env = env_int("GQA_CHUNK", 0);
   const bool target_env = env_int("GQA_TARGET_WGS", 0) > 0;
   const int fused_max = env_int("GQA_FUSED_MAX_SPLITS", kMaxFusedSplits);

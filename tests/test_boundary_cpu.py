@@ -119,7 +119,8 @@ def _decode_ws(B, H, S, d, grid=0):
 def test_split_plan_model(lib, monkeypatch):
     """Split lengths: about 256 workgroups (on the matrix cores the count
     that fills whole rounds of 256 best), at least 256 positions on the
-    matrix cores (32 on the VALU kernel), at least Lmax/256, at most 4096."""
+    matrix cores (32 on the VALU kernel), at least Lmax/256, at most 8192
+    on the matrix cores and 4096 on the VALU kernel."""
     for k in ("GQA_CHUNK", "GQA_TARGET_WGS", "GQA_MAX_CHUNK", "GQA_KERNEL", "GQA_HEAD_SPLIT", "GQA_MERGE", "GQA_ORDER",
               "GQA_FUSED_MAX_SPLITS"):
         monkeypatch.delenv(k, raising=False)
@@ -129,7 +130,8 @@ def test_split_plan_model(lib, monkeypatch):
         (1, 32, 8, 128, 4096, BF16, 16),      # 8 units: 256-position floor
         (4, 32, 8, 128, 4096, BF16, 8),       # 32 units: 512
         (1, 32, 8, 128, 32768, BF16, 32),     # 8 units, long: 1024 (256 WGs)
-        (64, 64, 8, 128, 32768, BF16, 8, 4096),  # 512 units: 4096 cap; 4096 workgroups, ordered
+        (64, 64, 8, 128, 32768, BF16, 4, 2048),  # 512 units: 8192 cap; 2048 workgroups, ordered
+        (64, 64, 8, 128, 32768, F32, 8, 4096),   # VALU: 4096 cap; 4096 workgroups, ordered
         (8, 32, 16, 128, 8192, BF16, 2),      # 128 units: 4096
         (1, 8, 2, 64, 256, F32, 8),           # VALU, 2 units: 32-position floor
         (1, 8, 2, 64, 8192, F32, 256),        # VALU, 2 units of 4 heads: 768 workgroups aimed at, 32-position splits
@@ -159,7 +161,7 @@ def test_split_plan_model(lib, monkeypatch):
     for B, H, G, d, L, dt, S, *grid in cases:
         assert lib.gqa_decode_workspace_size(B, H, G, d, L, dt) == _decode_ws(B, H, S, d, *grid), (B, H, G, d, L, dt, S)
     monkeypatch.setenv("GQA_ORDER", "0")  # no dispatch order: no order region
-    assert lib.gqa_decode_workspace_size(64, 64, 8, 128, 32768, BF16) == _decode_ws(64, 64, 8, 128)
+    assert lib.gqa_decode_workspace_size(64, 64, 8, 128, 32768, BF16) == _decode_ws(64, 64, 4, 128)
     # one split: no workspace
     assert lib.gqa_decode_workspace_size(32, 64, 8, 64, 2048, BF16) == 0
     assert lib.gqa_decode_workspace_size(128, 32, 1, 128, 1024, BF16) == 0  # 2 head chunks, one split each

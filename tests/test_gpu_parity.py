@@ -278,14 +278,17 @@ def test_default_plan_shapes(env, shape):
     check(out[rows], oracle_out(q, k, v, lt, scale, rows=rows), dtype, "plan shape %s" % (shape,))
 
 
-def test_very_long_sequence(env):
-    """2,097,152 positions: the 4096-position split cap gives 512 splits (more
-    than the planner's usual 256), merged by the wide kernel 16 per slice."""
+@pytest.mark.parametrize("cap", [None, 4096])
+def test_very_long_sequence(env, cap):
+    """2,097,152 positions: the default 8192-position split cap gives the
+    planner's usual 256 splits; a 4096 cap gives 512 (more than 256), merged
+    by the wide kernel 16 per slice."""
+    env(GQA_MAX_CHUNK=cap)
     w = wl.Workload("very_long", 1, 8, 1, 64, 1 << 21, "bf16", 43)
     q, k, v, lens = wl.make_inputs(w, DEV)
     out = run_gpu(q, k, v, lens, w.scale)
     ref = oracle_out(q, k, v, lens, w.scale)
-    check(out, ref, "bf16", "B1 H8 G1 d64 L2097152")
+    check(out, ref, "bf16", "B1 H8 G1 d64 L2097152 cap %s" % cap)
     check_relative(out, ref, "B1 H8 G1 d64 L2097152")
 
 
