@@ -147,6 +147,41 @@ gqa_status make_plan(int B, int H, int G, int d, int Lmax, gqa_dtype dt, Plan *p
     if (S > 1) e += 128.0 + (S > fused_max ? 128.0 : 4.0 * heads * S * (d + 2) * 4 / 1024);
     return e;
   };
+  // VALU kernel, grids of at most one round (256 workgroups): fewer, longer
+  // splits where the split protocol costs more than the shorter stream
+  // saves.  Estimated time in us: a workgroup streams ~40 KiB of K and V per
+  // us plus ~1 us fixed; a split plan adds ~2.5 us for the partial stores,
+  // arrival and in-kernel merge, plus ~0.2 us per split the merge reads
+  // (~5 us for the separate wide merge kernel).  Candidates: the target's
+  // split count halved down to 1.  Measured with HIP-graph replays, cold
+  // caches (split count: default -> chosen): B1 H8 G2 d64 L1024 f32
+  // 32 -> 8 splits 10.25 -> 8.31 us, B1 H32 G8 d128 L512 f32 16 -> 8
+  // 10.07 -> 8.90, B1 H16 G16 d128 L1024 bf16 16 -> 8 10.28 -> 8.15,
+  // B4 H32 G32 d64 L512 bf16 2 -> 1 8.45 -> 7.31, B1 H8 G2 d64 L256 f32
+  // 8 -> 1 8.31 -> 7.95; B2 H8 G2 d128 L2048 f32 keeps its 64 splits (12.99;
+  // 8 splits 18.69).
+  auto valu_chunk = [&](long units, int base) {
+    const long S0 = ceil_div(Lmax, base);
+    if (S0 <= 1 || units * S0 > 256) return base;
+    const double kib_per_pos = d * (dt == GQA_F32 ? 8.0 : 4.0) / 1024;
+    auto est = [&](int chunk) {
+      const long S = ceil_div(Lmax, chunk);
+      double e = chunk * kib_per_pos / 40.0 + 1.0;
+      if (S > 1) e += S > fused_max ? 5.0 : 2.5 + 0.2 * S;
+      return e;
+    };
+    int best = base;
+    double best_e = est(base);
+    for (long S = S0 / 2; S >= 1; S /= 2) {
+      const int c = chunk_of(S);
+      const double e = est(c);
+      if (e < best_e) {
+        best_e = e;
+        best = c;
+      }
+    }
+    return best;
+  };
   // Split length for a grid of `units` (b, g, head chunk) units of `heads`
   // query heads each: about `target` workgroups (one per compute unit).  On
   // the matrix cores the split count is then the one of lowest plan_cost
@@ -166,7 +201,8 @@ gqa_status make_plan(int B, int H, int G, int d, int Lmax, gqa_dtype dt, Plan *p
     // (only run there when forced) 768 is slower on the T5-XXL shapes.
     const long tgt = (kind == KIND_VALU && dt == GQA_F32 && heads >= 4 && !target_env) ? 768 : target;
     const int base = chunk_of((tgt + units - 1) / units);
-    if (kind != KIND_MFMA || target_env) return base;
+    if (target_env) return base;
+    if (kind != KIND_MFMA) return valu_chunk(units, base);
     const long s_max = ceil_div(Lmax, base) > fused_max ? ceil_div(Lmax, base) : (long)fused_max;
     auto est = [&](int chunk) { return plan_cost(units, heads, chunk); };
     int best = base;

@@ -133,7 +133,12 @@ def test_split_plan_model(lib, monkeypatch):
         (64, 64, 8, 128, 32768, BF16, 4, 2048),  # 512 units: 8192 cap; 2048 workgroups, ordered
         (64, 64, 8, 128, 32768, F32, 8, 4096),   # VALU: 4096 cap; 4096 workgroups, ordered
         (8, 32, 16, 128, 8192, BF16, 2),      # 128 units: 4096
-        (1, 8, 2, 64, 256, F32, 8),           # VALU, 2 units: 32-position floor
+        # VALU grids of one round: the target's split count halved while the
+        # estimate falls (fewer splits where the merge costs more than it saves)
+        (1, 8, 2, 64, 1024, F32, 8),          # 2 units: 32 -> 8 splits of 128
+        (1, 32, 8, 128, 512, F32, 8),         # 8 units: 16 -> 8 splits of 64
+        (1, 16, 16, 128, 1024, BF16, 8),      # r = 1 (VALU), 16 units: 16 -> 8 splits of 128
+        (2, 8, 2, 128, 2048, F32, 64),        # 4 units: keeps 64 splits of 32 (wide merge)
         (1, 8, 2, 64, 8192, F32, 256),        # VALU, 2 units of 4 heads: 768 workgroups aimed at, 32-position splits
         (1, 8, 1, 128, 131072, BF16, 256),    # one unit, long: 512-position splits (256 WGs)
         (1, 8, 1, 128, 262144, F32, 256),     # at most 256 splits: 1024 positions
@@ -163,6 +168,11 @@ def test_split_plan_model(lib, monkeypatch):
     monkeypatch.setenv("GQA_ORDER", "0")  # no dispatch order: no order region
     assert lib.gqa_decode_workspace_size(64, 64, 8, 128, 32768, BF16) == _decode_ws(64, 64, 4, 128)
     # one split: no workspace
+    assert lib.gqa_decode_workspace_size(1, 8, 2, 64, 256, F32) == 0     # VALU: 8 -> 1 split by the estimate
+    assert lib.gqa_decode_workspace_size(4, 32, 32, 64, 512, BF16) == 0  # VALU r = 1: 2 -> 1
+    monkeypatch.setenv("GQA_TARGET_WGS", "256")  # a plain target: 32-position floor, 8 splits
+    assert lib.gqa_decode_workspace_size(1, 8, 2, 64, 256, F32) == _decode_ws(1, 8, 8, 64)
+    monkeypatch.delenv("GQA_TARGET_WGS")
     assert lib.gqa_decode_workspace_size(32, 64, 8, 64, 2048, BF16) == 0
     assert lib.gqa_decode_workspace_size(128, 32, 1, 128, 1024, BF16) == 0  # 2 head chunks, one split each
 
