@@ -562,7 +562,7 @@ def main():
         return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (collectives and sharding are out of "
+        print("bench.py measures one GPU: the library has no multi-GPU path (collectives and sharding are out of "
               "scope); run with --gpus 1", file=sys.stderr)
         return 2
     if args.meanpool:
