@@ -199,7 +199,15 @@ gqa_status make_plan(int B, int H, int G, int d, int Lmax, gqa_dtype dt, Plan *p
     // 80.4 -> 44.0 us); with 1 or 2 heads one per compute unit stays best
     // (B8 H32 G16 d128 L8192: 154.3 us, 166.0 with 768), and on bfloat16
     // (only run there when forced) 768 is slower on the T5-XXL shapes.
-    const long tgt = (kind == KIND_VALU && dt == GQA_F32 && heads >= 4 && !target_env) ? 768 : target;
+    // With 4 heads per row set and the row ring, two workgroups per compute
+    // unit do as well where they divide evenly (units dividing 512): binary32
+    // Mistral-7B shape 93.1 -> 90.4 us, B4 H32 G8 d128 L8192 56.0 -> 50.6,
+    // B32 L1024 52.8 -> 49.7, B1 L32768 57.3 -> 53.1; where they would not
+    // (B12 L2048: 576 workgroups, 47.7 against 44.5 us with 768) and with 8
+    // heads per row set (B2 H64 G8 d128 L8192 58.7 against 50.5 us) 768 stays.
+    long tgt = target;
+    if (kind == KIND_VALU && dt == GQA_F32 && heads >= 4 && !target_env)
+      tgt = (heads == 4 && 512 % units == 0) ? 512 : 768;
     const int base = chunk_of((tgt + units - 1) / units);
     if (target_env) return base;
     if (kind != KIND_MFMA) return valu_chunk(units, base);
