@@ -141,6 +141,12 @@ def run_bench(args):
     from grouped_query_kv_decode_amd import workloads as wl
 
     w = wl.WORKLOADS[args.workload]
+    if args.dtype == "f32" and args.variant == "layer":
+        raise SystemExit("--variant layer runs the bf16 projections: use --dtype bf16")
+    if args.dtype and args.dtype != w.dtype:
+        # the same shape and seeds in the other storage type (binary32 runs on
+        # the VALU kernel); the name says which
+        w = w.with_(dtype=args.dtype, name=w.name.replace("_" + w.dtype + "_", "_" + args.dtype + "_"))
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     gqa.load_library()
@@ -533,6 +539,8 @@ def main():
     ap.add_argument("--workload", default="mistral7b_bf16_B16_H32_G8_d128_L4096")
     ap.add_argument("--rotate", type=int, default=0, help="input sets cycled through (default: >= 1 GiB of caches)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--dtype", choices=["bf16", "f32"], default=None,
+                    help="storage type of q, caches and output (default: the workload's)")
     ap.add_argument("--graph", action="store_true",
                     help="time one replay of the K steps captured into a HIP graph (no host launch cost)")
     ap.add_argument("--variant", choices=["decode", "append", "window", "layer"], default="decode",
