@@ -260,21 +260,29 @@ PLAN_SHAPES = [
     (4, 32, 1, 128, 16384, "bf16"),    # 32 heads per K/V head: 1 head chunk, 64 splits (wide merge)
     (64, 64, 1, 64, 4096, "bf16"),     # 64 heads per K/V head: 2 head chunks
     (12, 32, 8, 128, 2048, "f32"),     # binary32, VALU kernel aiming at 768 workgroups
+    (4, 32, 8, 128, 8192, "f32"),      # binary32, 32 units divide 512: 512 workgroups
+    (64, 32, 8, 128, 2048, "f32"),     # binary32, 512 units: one split each
+    (1, 8, 2, 64, 1024, "f32"),        # VALU one-round grid: 32 -> 8 splits by the estimate
+    (4, 32, 32, 64, 512, "bf16"),      # VALU (r = 1): 2 -> 1 split by the estimate
+    (64, 64, 8, 128, 16384, "bf16"),   # 8192-position split cap: 2 splits, 1024 workgroups
 ]
 
 
 @pytest.mark.parametrize("shape", PLAN_SHAPES, ids=lambda c: "B%d_H%d_G%d_d%d_L%d_%s" % c)
 def test_default_plan_shapes(env, shape):
-    """Shapes whose default plans come from the split-count, head-chunk and
-    binary32 target estimates, against the oracle on sampled sequences
-    (ragged lengths keep every split path busy)."""
+    """Shapes whose default plans come from the split-count, head-chunk,
+    binary32 target and VALU split estimates and the split cap, against the
+    oracle on sampled sequences (ragged lengths keep every split path busy)."""
     B, H, G, d, L, dtype = shape
     gen = torch.Generator().manual_seed(B * 131 + L)
     lens = [int(x) for x in torch.randint(1, L + 1, (B,), generator=gen)]
     lens[0] = L
     q, k, v, lt, scale = rand_case(B, H, G, d, L, lens, dtype, seed=90 + B)
     out = run_gpu(q, k, v, lt, scale)
-    rows = sorted(set([0, 1, B // 2, B - 1]))
+    # sampled sequences, all inside the batch (an index past it would make
+    # torch's gather read out of bounds on the device)
+    rows = sorted(set(r for r in (0, 1, B // 2, B - 1) if r < B))
+    assert all(0 <= r < B for r in rows)
     check(out[rows], oracle_out(q, k, v, lt, scale, rows=rows), dtype, "plan shape %s" % (shape,))
 
 
