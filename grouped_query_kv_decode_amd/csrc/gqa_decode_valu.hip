@@ -51,9 +51,15 @@ __device__ __forceinline__ float row_sum(float x) {
   return x;
 }
 
-template <typename T, int D, int RC, int U, bool SPEC>
+// VPL: 16-byte pieces a lane holds of each row (1, or 2 for binary32 rows
+// of 128 elements, which then span 16 lanes instead of 32: fewer cross-lane
+// reduction steps per score).  Piece v of every lane lies in the v-th 1/VPL
+// of the row, so each load instruction reads one contiguous run per row.
+template <typename T, int D, int RC, int U, bool SPEC, int VPL>
 __global__ __launch_bounds__(256) void decode_valu(DecodeParams p) {
-  constexpr int EPL = Elems<T>::kPerLane;  // elements per lane per row
+  constexpr int PPL = Elems<T>::kPerLane;  // elements per 16-byte piece
+  constexpr int EPL = PPL * VPL;           // elements per lane per row
+  constexpr int PSTRIDE = D / VPL;         // elements between a lane's pieces
   constexpr int LPR = D / EPL;             // lanes per row
   constexpr int RPW = 64 / LPR;            // rows per wave per load
   constexpr int NRG = 4 * RPW;             // row groups per workgroup
@@ -78,20 +84,22 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeParams p) {
   const int head0 = g * p.r + jbase;
   const bool append = p.k_new != nullptr;
   const size_t slab = ((size_t)b * p.G + g) * (size_t)p.Lmax * D;
-  const T *kp = static_cast<const T *>(p.k) + slab + sub * EPL;
-  const T *vp = static_cast<const T *>(p.v) + slab + sub * EPL;
+  const T *kp = static_cast<const T *>(p.k) + slab + sub * PPL;
+  const T *vp = static_cast<const T *>(p.v) + slab + sub * PPL;
 
   // Query rows of the served heads (they do not depend on the length).
-  uint4 qraw[RC];
+  uint4 qraw[RC][VPL];
 #pragma unroll
   for (int j = 0; j < RC; ++j)
-    qraw[j] = j < nh ? *reinterpret_cast<const uint4 *>(static_cast<const T *>(p.q) +
-                                                       ((size_t)b * p.H + head0 + j) * D + sub * EPL)
-                     : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int v = 0; v < VPL; ++v)
+      qraw[j][v] = j < nh ? *reinterpret_cast<const uint4 *>(static_cast<const T *>(p.q) +
+                                                            ((size_t)b * p.H + head0 + j) * D + sub * PPL + v * PSTRIDE)
+                          : make_uint4(0u, 0u, 0u, 0u);
 
   // A slot of rows: U rows per row group, their validity in the split.
   struct Rows {
-    uint4 kr[U], vr[U];
+    uint4 kr[U][VPL], vr[U][VPL];
     bool ok[U];
   };
   constexpr int kStep = NRG * U;
@@ -112,8 +120,11 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeParams p) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int row = min(ts_guess + u * NRG + rg, p.Lmax - 1);
-      first.kr[u] = stream_load(reinterpret_cast<const uint4 *>(kp + (size_t)row * D));
-      first.vr[u] = stream_load(reinterpret_cast<const uint4 *>(vp + (size_t)row * D));
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) {
+        first.kr[u][v] = stream_load(reinterpret_cast<const uint4 *>(kp + (size_t)row * D + v * PSTRIDE));
+        first.vr[u][v] = stream_load(reinterpret_cast<const uint4 *>(vp + (size_t)row * D + v * PSTRIDE));
+      }
     }
   }
 
@@ -135,13 +146,14 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeParams p) {
   float qf[RC][EPL];
 #pragma unroll
   for (int j = 0; j < RC; ++j) {
-    Elems<T>::widen(qraw[j], qf[j]);
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) Elems<T>::widen(qraw[j][v], qf[j] + v * PPL);
 #pragma unroll
     for (int e = 0; e < EPL; ++e) qf[j][e] *= p.scale_log2;
   }
 
-  const T *knew = append ? static_cast<const T *>(p.k_new) + ((size_t)b * p.G + g) * D + sub * EPL : nullptr;
-  const T *vnew = append ? static_cast<const T *>(p.v_new) + ((size_t)b * p.G + g) * D + sub * EPL : nullptr;
+  const T *knew = append ? static_cast<const T *>(p.k_new) + ((size_t)b * p.G + g) * D + sub * PPL : nullptr;
+  const T *vnew = append ? static_cast<const T *>(p.v_new) + ((size_t)b * p.G + g) * D + sub * PPL : nullptr;
 
   float m[RC], l[RC], o[RC][EPL];
 #pragma unroll
@@ -159,8 +171,11 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeParams p) {
       R.ok[u] = t < t1;
       const int row = R.ok[u] ? t : t1 - 1;  // never past the length
       const bool fresh = append && row == n - 1;
-      R.kr[u] = stream_load(reinterpret_cast<const uint4 *>(fresh ? knew : kp + (size_t)row * D));
-      R.vr[u] = stream_load(reinterpret_cast<const uint4 *>(fresh ? vnew : vp + (size_t)row * D));
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) {
+        R.kr[u][v] = stream_load(reinterpret_cast<const uint4 *>((fresh ? knew : kp + (size_t)row * D) + v * PSTRIDE));
+        R.vr[u][v] = stream_load(reinterpret_cast<const uint4 *>((fresh ? vnew : vp + (size_t)row * D) + v * PSTRIDE));
+      }
     }
   };
   // The speculative slot once the split is known: rows past it masked, with V zero.
@@ -168,18 +183,19 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeParams p) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       R.ok[u] = tb + u * NRG + rg < t1;
-      if (!R.ok[u]) R.vr[u] = make_uint4(0u, 0u, 0u, 0u);
+      if (!R.ok[u])
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) R.vr[u][v] = make_uint4(0u, 0u, 0u, 0u);
     }
   };
   auto process = [&](const Rows &R) {
-    const uint4 *kr = R.kr;
-    const uint4 *vr = R.vr;
     const bool *ok = R.ok;
     float sc[U][RC];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       float kf[EPL];
-      Elems<T>::widen(kr[u], kf);
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) Elems<T>::widen(R.kr[u][v], kf + v * PPL);
 #pragma unroll
       for (int j = 0; j < RC; ++j) {
         float acc = 0.f;
@@ -206,7 +222,8 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeParams p) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       float vf[EPL];
-      Elems<T>::widen(vr[u], vf);
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) Elems<T>::widen(R.vr[u][v], vf + v * PPL);
 #pragma unroll
       for (int j = 0; j < RC; ++j) {
         const float pj = fast_exp2(sc[u][j] - sh[j]);
@@ -301,8 +318,9 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeParams p) {
       for (int j = 0; j < RC; ++j)
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
+          const int x = (e / PPL) * PSTRIDE + sub * PPL + e % PPL;  // element of piece e / PPL
           const float add = o[j][e] * a_self[j];
-          sm_o[j][sub * EPL + e] = w == 0 ? add : sm_o[j][sub * EPL + e] + add;
+          sm_o[j][x] = w == 0 ? add : sm_o[j][x] + add;
         }
     }
     __syncthreads();
@@ -333,11 +351,26 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeParams p) {
 
 template <typename T, int D, int RC>
 hipError_t launch_t(const DecodeParams &p, unsigned grid, hipStream_t stream) {
-  constexpr int U = RC <= 4 ? 8 : 4;
+  // Two pieces per lane for binary32 rows of 128 elements serving 8 heads
+  // per row set (GQA_VALU_PIECES=1 restores one), with half the rows per slot
+  // (same bytes in flight): B2 H64 G8 d128 L8192 50.7 -> 46.0 us.  With 1 or
+  // 2 heads it measured neutral, with 4 heads 2-9% slower (Mistral-7B shape
+  // 87.8 -> 91.2 us), so those keep one piece.
+  constexpr int VPL = (std::is_same<T, float>::value && D == 128 && RC == 8) ? 2 : 1;
+  constexpr int U = (RC <= 4 ? 8 : 4) / VPL;
+  const char *env = getenv("GQA_VALU_PIECES");
+  if (VPL == 2 && env && env[0] == '1') {
+    constexpr int U1 = RC <= 4 ? 8 : 4;
+    if (grid <= 256 && p.k_new == nullptr)
+      hipLaunchKernelGGL((decode_valu<T, D, RC, U1, true, 1>), dim3(grid), dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL((decode_valu<T, D, RC, U1, false, 1>), dim3(grid), dim3(256), 0, stream, p);
+    return hipGetLastError();
+  }
   if (grid <= 256 && p.k_new == nullptr)
-    hipLaunchKernelGGL((decode_valu<T, D, RC, U, true>), dim3(grid), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((decode_valu<T, D, RC, U, true, VPL>), dim3(grid), dim3(256), 0, stream, p);
   else
-    hipLaunchKernelGGL((decode_valu<T, D, RC, U, false>), dim3(grid), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((decode_valu<T, D, RC, U, false, VPL>), dim3(grid), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
