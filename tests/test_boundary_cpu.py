@@ -139,6 +139,12 @@ def test_split_plan_model(lib, monkeypatch):
         (1, 32, 8, 128, 512, F32, 8),         # 8 units: 16 -> 8 splits of 64
         (1, 16, 16, 128, 1024, BF16, 8),      # r = 1 (VALU), 16 units: 16 -> 8 splits of 128
         (2, 8, 2, 128, 2048, F32, 64),        # 4 units: keeps 64 splits of 32 (wide merge)
+        # binary32, 4 heads per row set: 512 workgroups where the units divide
+        # 512, else 768; 8 heads per row set: 768
+        (4, 32, 8, 128, 8192, F32, 16),       # 32 units: 512 workgroups
+        (16, 32, 8, 128, 4096, F32, 4),       # 128 units: 512
+        (12, 32, 8, 128, 2048, F32, 8),       # 96 units do not divide 512: 768
+        (2, 64, 8, 128, 8192, F32, 43),       # 8 heads per row set: 768 aimed at, 192-position splits
         (1, 8, 2, 64, 8192, F32, 256),        # VALU, 2 units of 4 heads: 768 workgroups aimed at, 32-position splits
         (1, 8, 1, 128, 131072, BF16, 256),    # one unit, long: 512-position splits (256 WGs)
         (1, 8, 1, 128, 262144, F32, 256),     # at most 256 splits: 1024 positions
