@@ -474,6 +474,7 @@ def counter_mean(d, counter, kernel_substr):
     """Mean per-dispatch value of a rocprofv3 --pmc counter for kernels whose name contains kernel_substr."""
     vals = [float(r["Counter_Value"]) for r in _read_csvs(d, "counter_collection.csv")
             if r.get("Counter_Name") == counter and kernel_substr in r.get("Kernel_Name", "")]
+    vals += [v for (k, c, v) in _db_rows(d)[1] if c == counter and kernel_substr in k]
     if not vals:
         raise SystemExit("no %s samples for %s in %s" % (counter, kernel_substr, d))
     return sum(vals) / len(vals), len(vals)
@@ -509,10 +510,41 @@ def _read_csvs(d, suffix):
     return rows
 
 
+def _db_rows(d):
+    """(kernel durations, counter samples) from rocprofv3's SQLite output
+    (*_results.db, its default format): {name: [ns, ...]}, [(kernel, counter, value)]."""
+    import sqlite3
+    durs, ctr = {}, []
+    for f in sorted(glob.glob(os.path.join(d, "**", "*_results.db"), recursive=True)):
+        con = sqlite3.connect(f)
+        for name, dur in con.execute("select name, end - start from kernels"):
+            durs.setdefault(name, []).append(float(dur))
+        for kname, cname, val in con.execute("select kernel_name, counter_name, value from counters_collection"):
+            ctr.append((kname, cname, float(val)))
+        con.close()
+    return durs, ctr
+
+
 def summarize_rocprof(d):
-    """Per-kernel duration stats and per-dispatch counter means from rocprofv3 CSVs."""
+    """Per-kernel duration stats and per-dispatch counter means from rocprofv3
+    output (CSV files or the SQLite database)."""
     stats = _read_csvs(d, "kernel_stats.csv")
     out = []
+    durs, dbctr = _db_rows(d)
+    if durs:
+        out.append("kernel stats (rocprofv3 --kernel-trace, from the results database):")
+        out.append("%-90s %7s %10s %10s %10s %10s" % ("kernel", "calls", "avg_us", "median_us", "min_us", "max_us"))
+        for name, v in sorted(durs.items(), key=lambda kv: -sum(kv[1])):
+            v = sorted(v)
+            out.append("%-90s %7d %10.2f %10.2f %10.2f %10.2f" % (name[:90], len(v), sum(v) / len(v) / 1e3,
+                                                               v[len(v) // 2] / 1e3, v[0] / 1e3, v[-1] / 1e3))
+    if dbctr:
+        agg = {}
+        for kname, cname, val in dbctr:
+            agg.setdefault((kname, cname), []).append(val)
+        out.append("counters (rocprofv3 --pmc), mean per dispatch:")
+        for (kname, cname), vals in sorted(agg.items()):
+            out.append("%-90s %-12s n=%-5d mean=%.1f" % (kname[:90], cname, len(vals), sum(vals) / len(vals)))
     if stats:
         out.append("kernel stats (rocprofv3 --kernel-trace --stats):")
         out.append("%-90s %7s %12s %12s %12s" % ("kernel", "calls", "avg_us", "min_us", "max_us"))

@@ -19,6 +19,7 @@ Entry points (same names as the C ABI, without the ``gqa_`` prefix):
     meanpool_kv(w, H, G, out=None)
     decode_kernel_kind(B, H, G, d, Lmax, dtype)
     stream_read(buf, nontemporal=True, grid=0, sink=None)   the read-ceiling probe (measurement only)
+    tuning_reload()                    re-read the GQA_* launch-plan overrides (tuning and tests)
 """
 from __future__ import annotations
 
@@ -28,7 +29,7 @@ import os
 __all__ = [
     "GQAError", "decode", "decode_phase", "decode_window", "decode_append", "decode_workspace_size", "workspace_init", "meanpool_kv",
     "linear", "linear_workspace_size", "pack_weight", "linear_packed", "decode_layer", "decode_layer_workspace_size", "LayerStep",
-    "decode_kernel_kind", "stream_read", "status_string", "library_path", "load_library", "Decoder",
+    "decode_kernel_kind", "stream_read", "tuning_reload", "status_string", "library_path", "load_library", "Decoder",
     "GQA_F32", "GQA_BF16",
 ]
 
@@ -45,7 +46,7 @@ EXPORTED = [
     "gqa_decode_append", "gqa_linear_workspace_size", "gqa_linear", "gqa_pack_weight", "gqa_linear_packed",
     "gqa_decode_layer_workspace_size",
     "gqa_decode_layer", "gqa_meanpool_kv",
-    "gqa_status_string", "gqa_last_hip_error", "gqa_decode_kernel_kind", "gqa_stream_read",
+    "gqa_status_string", "gqa_last_hip_error", "gqa_decode_kernel_kind", "gqa_stream_read", "gqa_tuning_reload",
 ]
 
 _lib = None
@@ -110,9 +111,17 @@ def load_library(path: str | None = None):
     lib.gqa_decode_kernel_kind.argtypes = [ci, ci, ci, ci, ci, ci]
     lib.gqa_stream_read.restype = ci
     lib.gqa_stream_read.argtypes = [vp, sz, ci, ci, vp, vp]
+    lib.gqa_tuning_reload.restype = None
+    lib.gqa_tuning_reload.argtypes = []
     if path is None:
         _lib = lib
     return lib
+
+
+def tuning_reload() -> None:
+    """Re-read the GQA_* launch-plan overrides from the environment (the
+    library reads them once when it loads; see include/gqa_measure.h)."""
+    load_library().gqa_tuning_reload()
 
 
 def status_string(status: int) -> str:

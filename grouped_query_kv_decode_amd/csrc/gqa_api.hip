@@ -4,15 +4,19 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
 #include <string>
 
 #include "gqa.h"
+#include "gqa_measure.h"
 #include "gqa_device.h"
 #include "gqa_linear.h"
 
 namespace {
 
 thread_local std::string g_last_hip_error;
+
+enum { KIND_VALU = 0, KIND_MFMA = 1 };
 
 gqa_status hip_fail(hipError_t e) {
   g_last_hip_error = hipGetErrorString(e);
@@ -27,6 +31,60 @@ int env_int(const char *name, int dflt) {
   return (end && *end == 0 && x > 0 && x < (1L << 30)) ? (int)x : dflt;
 }
 
+bool env_is(const char *name, const char *value) {
+  const char *v = getenv(name);
+  return v && strcmp(v, value) == 0;
+}
+
+// Launch-plan overrides for tuning and tests.  They are read from the
+// environment once, when the library is loaded, and again only on
+// gqa_tuning_reload(); a decode call never reads the environment, so the
+// plan a call takes cannot change between gqa_decode_workspace_size and the
+// call.  Zero (or -1) means "the measured default plan".
+struct Tuning {
+  int kernel;        // GQA_KERNEL=valu|mfma: 1 + KIND_VALU / 1 + KIND_MFMA, 0 the plan's choice
+  int target_wgs;    // GQA_TARGET_WGS: plain workgroup target (split count rounded up to it)
+  int max_chunk;     // GQA_MAX_CHUNK: split length cap
+  int chunk;         // GQA_CHUNK: split length
+  int fused_max;     // GQA_FUSED_MAX_SPLITS: splits merged inside the decode kernel at most
+  int waves;         // GQA_WAVES=8|16: matrix-core workgroup waves
+  int head_split;    // GQA_HEAD_SPLIT=1|2|4
+  int contig;        // GQA_CONTIG=1: contiguous per-wave tile runs
+  int temporal;      // GQA_TEMPORAL=0|1: non-temporal / plain cache loads (-1: the plan's)
+  int merge_kernel;  // GQA_MERGE=kernel
+  int order;         // GQA_ORDER=0|1 (-1: the plan's)
+  int valu_pieces;   // GQA_VALU_PIECES=1: one 16-byte piece per lane and row
+  int linear_waves, linear_ksplit, linear_tpi, linear_strips;  // GQA_LINEAR_*
+  int linear_unroll;                                           // GQA_LINEAR_UNROLL=0: 0, else -1
+};
+
+Tuning read_tuning() {
+  Tuning t;
+  t.kernel = env_is("GQA_KERNEL", "valu") ? 1 + KIND_VALU : (env_is("GQA_KERNEL", "mfma") ? 1 + KIND_MFMA : 0);
+  t.target_wgs = env_int("GQA_TARGET_WGS", 0);
+  t.max_chunk = env_int("GQA_MAX_CHUNK", 0);
+  t.chunk = env_int("GQA_CHUNK", 0);
+  t.fused_max = env_int("GQA_FUSED_MAX_SPLITS", 0);
+  t.waves = env_int("GQA_WAVES", 0);
+  t.head_split = env_int("GQA_HEAD_SPLIT", 0);
+  t.contig = env_int("GQA_CONTIG", 0) == 1;
+  const char *tmp = getenv("GQA_TEMPORAL");
+  t.temporal = tmp && tmp[0] ? (tmp[0] == '1') : -1;
+  t.merge_kernel = env_is("GQA_MERGE", "kernel");
+  t.order = env_is("GQA_ORDER", "0") ? 0 : (env_is("GQA_ORDER", "1") ? 1 : -1);
+  const char *pieces = getenv("GQA_VALU_PIECES");
+  t.valu_pieces = pieces && pieces[0] == '1';
+  t.linear_waves = env_int("GQA_LINEAR_WAVES", 0);
+  t.linear_ksplit = env_int("GQA_LINEAR_KSPLIT", 0);
+  t.linear_tpi = env_int("GQA_LINEAR_TPI", 0);
+  t.linear_strips = env_int("GQA_LINEAR_STRIPS", 0);
+  t.linear_unroll = env_is("GQA_LINEAR_UNROLL", "0") ? 0 : -1;
+  return t;
+}
+
+Tuning g_tuning = read_tuning();              // at library load
+std::atomic<unsigned> g_tuning_gen{1};        // bumped by gqa_tuning_reload: cached plans go stale
+
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
 int next_pow2(int x) {
@@ -35,7 +93,6 @@ int next_pow2(int x) {
   return p;
 }
 
-enum { KIND_VALU = 0, KIND_MFMA = 1 };
 
 // Workspace layout when some sequence may span several splits:
 //   [0, kCounterBytes)  arrival counters, one per (b, g, head chunk) unit;
@@ -59,6 +116,9 @@ struct Plan {
   int fused;
   int wide;     // merge by the wide merge kernel
   int ordered;  // workgroups take their items largest first (order region of the workspace)
+  int nontemporal;  // matrix-core cache loads non-temporal (plain when head chunks share lines)
+  int contig;       // matrix-core tiles as contiguous per-wave runs (tuning only)
+  int valu_pieces;  // VALU kernel forced to one 16-byte piece per lane and row (tuning only)
   unsigned grid;
   size_t ml_off, o_off, order_off, ws_bytes;
 };
@@ -101,23 +161,22 @@ gqa_status check_shape(int B, int H, int G, int d, int Lmax, gqa_dtype dt) {
 //  - grids of more than 1024 workgroups with at least 4 splits per sequence
 //    (several dispatch rounds) take their items largest first, in an order a
 //    small kernel sorts from the lengths on the device (GQA_ORDER=0/1).
-gqa_status make_plan(int B, int H, int G, int d, int Lmax, gqa_dtype dt, Plan *pl) {
+gqa_status make_plan(int B, int H, int G, int d, int Lmax, gqa_dtype dt, const Tuning &tu, Plan *pl) {
   const int r = H / G;
-  const char *force = getenv("GQA_KERNEL");
   int kind = (dt == GQA_BF16 && r >= 2 && r <= 64) ? KIND_MFMA : KIND_VALU;
-  if (force && strcmp(force, "valu") == 0) kind = KIND_VALU;
-  if (force && strcmp(force, "mfma") == 0 && dt == GQA_BF16 && r <= 64) kind = KIND_MFMA;
+  if (tu.kernel == 1 + KIND_VALU) kind = KIND_VALU;
+  if (tu.kernel == 1 + KIND_MFMA && dt == GQA_BF16 && r <= 64) kind = KIND_MFMA;
   pl->kind = kind;
   pl->NW = 4;
-  const int target = env_int("GQA_TARGET_WGS", 256);
+  const int target = tu.target_wgs > 0 ? tu.target_wgs : 256;
   // Split cap: 8192 positions on the matrix cores, measured against 4096 and
   // 6144 (ragged B64 H64 G8 d128 Lmax 32768 715 -> 707 us, B64 H64 G8 L16384
   // 664 -> 652 us, B32 H64 G8 L8192 164.5 -> 159 us, B8 H32 G8 L131072
   // 652 -> 641 us, no shape slower; 6144 leaves odd round counts).
-  const int max_chunk = env_int("GQA_MAX_CHUNK", kind == KIND_MFMA ? 8192 : 4096);
-  const int chunk_env = env_int("GQA_CHUNK", 0);
-  const bool target_env = env_int("GQA_TARGET_WGS", 0) > 0;
-  const int fused_max = env_int("GQA_FUSED_MAX_SPLITS", kMaxFusedSplits);
+  const int max_chunk = tu.max_chunk > 0 ? tu.max_chunk : (kind == KIND_MFMA ? 8192 : 4096);
+  const int chunk_env = tu.chunk;
+  const bool target_env = tu.target_wgs > 0;
+  const int fused_max = tu.fused_max > 0 ? tu.fused_max : kMaxFusedSplits;
   // Split length for about S splits: the floors (the matrix-core kernel's 4
   // waves take 8 tiles of 32 positions per 256, and shorter splits cost more
   // in epilogue and merge than they gain; the VALU kernel's rows are
@@ -259,7 +318,7 @@ gqa_status make_plan(int B, int H, int G, int d, int Lmax, gqa_dtype dt, Plan *p
       const int other = fit(hc / 2);  // at most two head blocks per workgroup (four measured slower)
       if (other != hc && hb_all / other <= 2 && cost(other) < cost(hc)) hc = other;
     }
-    const int hc_env = env_int("GQA_HEAD_SPLIT", 0);
+    const int hc_env = tu.head_split;
     if (hc_env == 1 || hc_env == 2 || hc_env == 4) hc = fit(hc_env > hb_all ? hb_all : hc_env);
     pl->HC = hc;
     pl->HB = hb_all / hc;
@@ -279,19 +338,18 @@ gqa_status make_plan(int B, int H, int G, int d, int Lmax, gqa_dtype dt, Plan *p
     // budget of the larger workgroup.
     const int nw_max = (pl->HB == 1 && d == 64) ? 16 : (pl->HB <= 2 ? 8 : 4);
     const int nw_def = 4;
-    const int nw = env_int("GQA_WAVES", nw_def);
+    const int nw = tu.waves > 0 ? tu.waves : nw_def;
     pl->NW = (nw == 8 || nw == 16) && nw <= nw_max ? nw : 4;
   }
   pl->S = ceil_div(Lmax, chunk);
   const unsigned long long grid = (unsigned long long)units * pl->S;
   if (grid == 0 || grid > 0x7fffffffULL) return GQA_ERR_SIZE;
   pl->grid = (unsigned)grid;
-  const char *merge = getenv("GQA_MERGE");
   // In-kernel merge: one counter per unit, and a merging workgroup that
   // reads every split of its heads, which pays up to kMaxFusedSplits; beyond
   // that a merge kernel spread over heads, dimensions and splits.
   pl->wide = pl->S > fused_max;
-  pl->fused = units <= kMaxFusedUnits && !pl->wide && !(merge && strcmp(merge, "kernel") == 0);
+  pl->fused = units <= kMaxFusedUnits && !pl->wide && !tu.merge_kernel;
   // Grids of several rounds with at least kOrderMinSplits splits per
   // sequence: the order kernel sorts the items largest first (ragged lengths
   // otherwise leave whole splits of the longest sequences to the last round:
@@ -299,9 +357,11 @@ gqa_status make_plan(int B, int H, int G, int d, int Lmax, gqa_dtype dt, Plan *p
   // each workgroup one dependent load at its start, ~1% on a batch of equal
   // lengths (B64 H32 G16 d128 L8192, 2 splits: 646.7 -> 654.6 us), hence the
   // split floor.
-  const char *ord = getenv("GQA_ORDER");
-  pl->ordered = (pl->S >= kOrderMinSplits && pl->grid > kOrderMinGrid && !(ord && strcmp(ord, "0") == 0)) ||
-                (ord && strcmp(ord, "1") == 0 && pl->S > 1);
+  pl->ordered = (pl->S >= kOrderMinSplits && pl->grid > kOrderMinGrid && tu.order != 0) || (tu.order == 1 && pl->S > 1);
+  // Cache loads: non-temporal, or plain where head chunks share the lines in L2.
+  pl->nontemporal = tu.temporal >= 0 ? !tu.temporal : pl->HC == 1 || kind != KIND_MFMA;
+  pl->contig = tu.contig;
+  pl->valu_pieces = tu.valu_pieces;
   if (pl->S > 1) {
     pl->ml_off = kCounterBytes;
     pl->o_off = pl->ml_off + round_up((size_t)B * H * pl->S * sizeof(float2), 256);
@@ -312,6 +372,33 @@ gqa_status make_plan(int B, int H, int G, int d, int Lmax, gqa_dtype dt, Plan *p
     pl->ml_off = pl->o_off = pl->order_off = pl->ws_bytes = 0;
   }
   return GQA_OK;
+}
+
+// Plans of the last few shapes each host thread used, keyed by the shape and
+// the tuning generation (a serving loop repeats a handful of shapes; the
+// plan then costs a lookup instead of the estimates).
+struct PlanEntry {
+  int B, H, G, d, Lmax, dt;
+  unsigned gen;  // 0: empty
+  gqa_status st;
+  Plan plan;
+};
+constexpr int kPlanCache = 8;
+thread_local PlanEntry t_plans[kPlanCache];
+thread_local unsigned t_plan_next;
+
+gqa_status get_plan(int B, int H, int G, int d, int Lmax, gqa_dtype dt, Plan *pl) {
+  const unsigned gen = g_tuning_gen.load(std::memory_order_acquire);
+  for (const PlanEntry &e : t_plans) {
+    if (e.gen == gen && e.B == B && e.H == H && e.G == G && e.d == d && e.Lmax == Lmax && e.dt == (int)dt) {
+      *pl = e.plan;
+      return e.st;
+    }
+  }
+  const gqa_status st = make_plan(B, H, G, d, Lmax, dt, g_tuning, pl);
+  PlanEntry &e = t_plans[t_plan_next++ % kPlanCache];
+  e = PlanEntry{B, H, G, d, Lmax, (int)dt, gen, st, *pl};
+  return st;
 }
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -336,10 +423,11 @@ gqa_status check_linear(int M, int K, int N, gqa_dtype dt) {
 }
 
 gqa_status make_linear_plan(int M, int K, int N, LinearPlan *pl) {
+  const Tuning &tu = g_tuning;
   const int ntile = N / 128;
   const int ksteps = K / 32;
-  pl->NW = env_int("GQA_LINEAR_WAVES", 4) == 8 ? 8 : 4;
-  int KS = env_int("GQA_LINEAR_KSPLIT", 0);
+  pl->NW = tu.linear_waves == 8 ? 8 : 4;
+  int KS = tu.linear_ksplit;
   if (KS == 0) {
     const int max_ks = ksteps / (2 * pl->NW);
     KS = 1;
@@ -355,7 +443,7 @@ gqa_status make_linear_plan(int M, int K, int N, LinearPlan *pl) {
   pl->TPI = per_wave >= 3 ? 4 : per_wave;
   if (pl->TPI < 1) pl->TPI = 1;
   if (pl->TPI > max_tpi) pl->TPI = max_tpi;
-  const int tpi_env = env_int("GQA_LINEAR_TPI", 0);
+  const int tpi_env = tu.linear_tpi;
   if (tpi_env == 1 || tpi_env == 2 || (tpi_env == 4 && max_tpi == 4)) pl->TPI = tpi_env;
   const unsigned long long grid = (unsigned long long)ntile * pl->KS;
   if (grid == 0 || grid > 0x7fffffffULL || ntile > kMaxFusedUnits) return GQA_ERR_SIZE;
@@ -435,13 +523,12 @@ gqa_status packed_impl(const void *x, const void *wp, void *const y[3], const in
   if (tb == 1) {
     for (int cand : {4, 2})
       if (sw == 1 && nstrips % cand == 0 && nstrips / cand >= 192) sw = cand;
-    const int sw_env = env_int("GQA_LINEAR_STRIPS", 0);
+    const int sw_env = g_tuning.linear_strips;
     if ((sw_env == 1 || sw_env == 2 || sw_env == 4) && nstrips % sw_env == 0) sw = sw_env;
   }
   const int kc = gqa::linear_packed_chunk_blocks(tb, sw);
   const int nch = (K / 32) % kc == 0 ? K / 32 / kc : 0;
-  const bool unroll = tb == 1 && sw <= 2 && (nch == 4 || nch == 8 || nch == 16) &&
-                      !(getenv("GQA_LINEAR_UNROLL") && strcmp(getenv("GQA_LINEAR_UNROLL"), "0") == 0);
+  const bool unroll = tb == 1 && sw <= 2 && (nch == 4 || nch == 8 || nch == 16) && g_tuning.linear_unroll != 0;
   const hipError_t e = gqa::launch_linear_packed(p, tb, sw, unroll ? nch : 0, stream);
   return e == hipSuccess ? GQA_OK : hip_fail(e);
 }
@@ -457,7 +544,7 @@ gqa_status make_layer_plan(int B, int H, int G, int d, int Lmax, int window, int
   (void)d_model;
   Plan ap;
   const int Leff = (window > 0 && window < Lmax) ? window : Lmax;
-  gqa_status st = make_plan(B, H, G, d, Leff, GQA_BF16, &ap);
+  gqa_status st = get_plan(B, H, G, d, Leff, GQA_BF16, &ap);
   if (st != GQA_OK) return st;
   // The counter region stays reserved even when the attention needs no
   // split: a workspace may be shared with other calls, which rely on its
@@ -479,15 +566,20 @@ extern "C" {
 size_t gqa_decode_workspace_size(int B, int H, int G, int d, int Lmax, gqa_dtype dtype) {
   if (check_shape(B, H, G, d, Lmax, dtype) != GQA_OK || B == 0) return 0;
   Plan pl;
-  if (make_plan(B, H, G, d, Lmax, dtype, &pl) != GQA_OK) return 0;
+  if (get_plan(B, H, G, d, Lmax, dtype, &pl) != GQA_OK) return 0;
   return pl.ws_bytes;
 }
 
 int gqa_decode_kernel_kind(int B, int H, int G, int d, int Lmax, gqa_dtype dtype) {
   if (check_shape(B, H, G, d, Lmax, dtype) != GQA_OK) return -1;
   Plan pl;
-  if (make_plan(B > 0 ? B : 1, H, G, d, Lmax, dtype, &pl) != GQA_OK) return -1;
+  if (get_plan(B > 0 ? B : 1, H, G, d, Lmax, dtype, &pl) != GQA_OK) return -1;
   return pl.kind;
+}
+
+void gqa_tuning_reload(void) {
+  g_tuning = read_tuning();
+  g_tuning_gen.fetch_add(1, std::memory_order_acq_rel);
 }
 
 gqa_status gqa_workspace_init(void *workspace, size_t workspace_bytes, hipStream_t stream) {
@@ -522,7 +614,7 @@ gqa_status decode_impl(int phase, const void *q, const void *k_new, const void *
   // a window shorter than the cache plans splits over the window only
   const int Leff = (window > 0 && window < Lmax) ? window : Lmax;
   Plan pl;
-  st = make_plan(B, H, G, d, Leff, dtype, &pl);
+  st = get_plan(B, H, G, d, Leff, dtype, &pl);
   if (st != GQA_OK) return st;
   if (pl.ws_bytes > 0) {
     if (!workspace) return GQA_ERR_NULL;
@@ -545,7 +637,7 @@ gqa_status decode_impl(int phase, const void *q, const void *k_new, const void *
   int *order = pl.ordered ? reinterpret_cast<int *>(ws + pl.order_off) : nullptr;
   p.order = order;
   p.fused = pl.fused;
-  p.contig = env_int("GQA_CONTIG", 0) == 1;
+  p.contig = pl.contig;
   p.B = B;
   p.H = H;
   p.G = G;
@@ -562,8 +654,9 @@ gqa_status decode_impl(int phase, const void *q, const void *k_new, const void *
     if (e != hipSuccess) return hip_fail(e);
   }
   if (phase != 2) {
-    const hipError_t e = pl.kind == KIND_MFMA ? gqa::launch_decode_mfma(p, d, pl.HB, pl.NW, pl.grid, stream)
-                                              : gqa::launch_decode_valu(p, (int)dtype, d, pl.RC, pl.grid, stream);
+    const hipError_t e =
+        pl.kind == KIND_MFMA ? gqa::launch_decode_mfma(p, d, pl.HB, pl.NW, pl.nontemporal, pl.grid, stream)
+                             : gqa::launch_decode_valu(p, (int)dtype, d, pl.RC, pl.valu_pieces, pl.grid, stream);
     if (e != hipSuccess) return hip_fail(e);
   }
   if (phase != 1 && pl.S > 1 && !pl.fused) {

@@ -258,14 +258,16 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma(DecodeParams p) {
       const float sh = safe_shift(m[hb]);
       float pv[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        pv[u] = fast_exp2(sc[u] - sh);
-        l[hb] += pv[u];
-      }
+      for (int u = 0; u < 8; ++u) pv[u] = fast_exp2(sc[u] - sh);
+      // The weights enter p.V rounded to bfloat16; the weight sum adds those
+      // same rounded values (widening bfloat16 is exact), so the output is a
+      // convex combination of value rows: a constant V comes back exactly.
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const bf16x2 t2 = {(__bf16)pv[2 * k], (__bf16)pv[2 * k + 1]};  // round to nearest even
-        pB[hb][k] = __builtin_bit_cast(unsigned, t2);
+        const unsigned bits = __builtin_bit_cast(unsigned, t2);
+        pB[hb][k] = bits;
+        l[hb] += __uint_as_float(bits << 16) + __uint_as_float(bits & 0xffff0000u);
       }
     }
     pv_steps<0, DB, HB>(o, T.vR, pB);
@@ -436,11 +438,9 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma(DecodeParams p) {
 }
 
 template <int D, int HB, int NW>
-hipError_t launch_t(const DecodeParams &p, unsigned grid, hipStream_t stream) {
-  const char *env = getenv("GQA_TEMPORAL");
-  const bool temporal = env && env[0] ? env[0] == '1' : p.HC > 1;
+hipError_t launch_t(const DecodeParams &p, bool nontemporal, unsigned grid, hipStream_t stream) {
   if constexpr (HB <= 2) {
-    if (temporal) {
+    if (!nontemporal) {
       hipLaunchKernelGGL((decode_mfma<D, HB, NW, false>), dim3(grid), dim3(64 * NW), 0, stream, p);
       return hipGetLastError();
     }
@@ -452,30 +452,32 @@ hipError_t launch_t(const DecodeParams &p, unsigned grid, hipStream_t stream) {
 // Larger workgroups only where the register budget (64 KiB per SIMD split
 // over more waves) holds the head blocks without spilling.
 template <int D, int HB>
-hipError_t launch_nw(const DecodeParams &p, int NW, unsigned grid, hipStream_t stream) {
+hipError_t launch_nw(const DecodeParams &p, int NW, bool nt, unsigned grid, hipStream_t stream) {
   if constexpr (HB == 1 && D == 64) {
-    if (NW == 16) return launch_t<D, HB, 16>(p, grid, stream);
+    if (NW == 16) return launch_t<D, HB, 16>(p, nt, grid, stream);
   }
   if constexpr (HB <= 2) {
-    if (NW == 8) return launch_t<D, HB, 8>(p, grid, stream);
+    if (NW == 8) return launch_t<D, HB, 8>(p, nt, grid, stream);
   }
-  return launch_t<D, HB, 4>(p, grid, stream);
+  return launch_t<D, HB, 4>(p, nt, grid, stream);
 }
 
 template <int D>
-hipError_t launch_hb(const DecodeParams &p, int HB, int NW, unsigned grid, hipStream_t stream) {
+hipError_t launch_hb(const DecodeParams &p, int HB, int NW, bool nt, unsigned grid, hipStream_t stream) {
   switch (HB) {
-    case 1: return launch_nw<D, 1>(p, NW, grid, stream);
-    case 2: return launch_nw<D, 2>(p, NW, grid, stream);
-    case 4: return launch_nw<D, 4>(p, NW, grid, stream);
+    case 1: return launch_nw<D, 1>(p, NW, nt, grid, stream);
+    case 2: return launch_nw<D, 2>(p, NW, nt, grid, stream);
+    case 4: return launch_nw<D, 4>(p, NW, nt, grid, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-hipError_t launch_decode_mfma(const DecodeParams &p, int D, int HB, int NW, unsigned grid, hipStream_t stream) {
-  return D == 64 ? launch_hb<64>(p, HB, NW, grid, stream) : launch_hb<128>(p, HB, NW, grid, stream);
+hipError_t launch_decode_mfma(const DecodeParams &p, int D, int HB, int NW, int nontemporal, unsigned grid,
+                              hipStream_t stream) {
+  const bool nt = nontemporal != 0;
+  return D == 64 ? launch_hb<64>(p, HB, NW, nt, grid, stream) : launch_hb<128>(p, HB, NW, nt, grid, stream);
 }
 
 }  // namespace gqa

@@ -350,7 +350,7 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeParams p) {
 }
 
 template <typename T, int D, int RC>
-hipError_t launch_t(const DecodeParams &p, unsigned grid, hipStream_t stream) {
+hipError_t launch_t(const DecodeParams &p, bool one_piece, unsigned grid, hipStream_t stream) {
   // Two pieces per lane for binary32 rows of 128 elements serving 8 heads
   // per row set (GQA_VALU_PIECES=1 restores one), with half the rows per slot
   // (same bytes in flight): B2 H64 G8 d128 L8192 50.7 -> 46.0 us.  With 1 or
@@ -358,8 +358,7 @@ hipError_t launch_t(const DecodeParams &p, unsigned grid, hipStream_t stream) {
   // 87.8 -> 91.2 us), so those keep one piece.
   constexpr int VPL = (std::is_same<T, float>::value && D == 128 && RC == 8) ? 2 : 1;
   constexpr int U = (RC <= 4 ? 8 : 4) / VPL;
-  const char *env = getenv("GQA_VALU_PIECES");
-  if (VPL == 2 && env && env[0] == '1') {
+  if (VPL == 2 && one_piece) {
     constexpr int U1 = RC <= 4 ? 8 : 4;
     if (grid <= 256 && p.k_new == nullptr)
       hipLaunchKernelGGL((decode_valu<T, D, RC, U1, true, 1>), dim3(grid), dim3(256), 0, stream, p);
@@ -375,21 +374,24 @@ hipError_t launch_t(const DecodeParams &p, unsigned grid, hipStream_t stream) {
 }
 
 template <typename T, int D>
-hipError_t launch_rc(const DecodeParams &p, int RC, unsigned grid, hipStream_t stream) {
+hipError_t launch_rc(const DecodeParams &p, int RC, bool one_piece, unsigned grid, hipStream_t stream) {
   switch (RC) {
-    case 1: return launch_t<T, D, 1>(p, grid, stream);
-    case 2: return launch_t<T, D, 2>(p, grid, stream);
-    case 4: return launch_t<T, D, 4>(p, grid, stream);
-    case 8: return launch_t<T, D, 8>(p, grid, stream);
+    case 1: return launch_t<T, D, 1>(p, one_piece, grid, stream);
+    case 2: return launch_t<T, D, 2>(p, one_piece, grid, stream);
+    case 4: return launch_t<T, D, 4>(p, one_piece, grid, stream);
+    case 8: return launch_t<T, D, 8>(p, one_piece, grid, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-hipError_t launch_decode_valu(const DecodeParams &p, int dtype, int D, int RC, unsigned grid, hipStream_t stream) {
-  if (dtype == 0) return D == 64 ? launch_rc<float, 64>(p, RC, grid, stream) : launch_rc<float, 128>(p, RC, grid, stream);
-  return D == 64 ? launch_rc<__bf16, 64>(p, RC, grid, stream) : launch_rc<__bf16, 128>(p, RC, grid, stream);
+hipError_t launch_decode_valu(const DecodeParams &p, int dtype, int D, int RC, int one_piece, unsigned grid,
+                              hipStream_t stream) {
+  const bool op = one_piece != 0;
+  if (dtype == 0)
+    return D == 64 ? launch_rc<float, 64>(p, RC, op, grid, stream) : launch_rc<float, 128>(p, RC, op, grid, stream);
+  return D == 64 ? launch_rc<__bf16, 64>(p, RC, op, grid, stream) : launch_rc<__bf16, 128>(p, RC, op, grid, stream);
 }
 
 }  // namespace gqa

@@ -196,8 +196,13 @@ __device__ void merge_heads(const DecodeParams &p, int b, int head0, int nh, int
 }
 
 // Host-side launchers (one per kernel translation unit).
-hipError_t launch_decode_valu(const DecodeParams &p, int dtype, int D, int RC, unsigned grid, hipStream_t stream);
-hipError_t launch_decode_mfma(const DecodeParams &p, int D, int HB, int NW, unsigned grid, hipStream_t stream);
+// one_piece (tuning): a 16-byte piece per lane and row also where the plan takes two.
+hipError_t launch_decode_valu(const DecodeParams &p, int dtype, int D, int RC, int one_piece, unsigned grid,
+                              hipStream_t stream);
+// nontemporal: the cache stream's loads are non-temporal (plain loads when
+// head chunks read the same lines; four head blocks always stream).
+hipError_t launch_decode_mfma(const DecodeParams &p, int D, int HB, int NW, int nontemporal, unsigned grid,
+                              hipStream_t stream);
 hipError_t launch_merge(const DecodeParams &p, int dtype, int D, int heads_per_unit, hipStream_t stream);
 hipError_t launch_merge_wide(const DecodeParams &p, int dtype, int D, hipStream_t stream);
 hipError_t launch_order(const DecodeParams &p, bool valu_layout, unsigned grid, int *order, hipStream_t stream);

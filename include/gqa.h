@@ -103,13 +103,14 @@ gqa_status gqa_workspace_init(void *workspace, size_t workspace_bytes, hipStream
  * (with few (sequence, K/V head) units, the group's heads are spread over 2
  * or 4 workgroups that read the same part); when a sequence spans several
  * splits (at most 256), the workgroup that finishes its unit last merges the
- * split results (log-sum-exp) into out.  Beyond 32 splits per sequence, above
- * 65536 units, or with the environment variable GQA_MERGE=kernel, a second
- * kernel does that merge instead (beyond 32 splits one spread over
- * sequences, heads, dimensions and slices of the splits).  Grids of more than
- * 1024 workgroups with at least 4 splits per sequence are preceded by a
- * one-workgroup kernel that orders their work items largest first (from
- * seq_lens, on the device; the outputs do not depend on it).  The call
+ * split results (log-sum-exp) into out.  Beyond 32 splits per sequence or
+ * above 65536 units a second kernel does that merge instead (beyond 32
+ * splits one spread over sequences, heads, dimensions and slices of the
+ * splits).  Grids of more than 1024 workgroups with at least 4 splits per
+ * sequence are preceded by a one-workgroup kernel that orders their work
+ * items largest first (from seq_lens, on the device; the outputs do not
+ * depend on it).  The launch plan depends only on the shape and dtype (and
+ * on the tuning overrides of gqa_measure.h, read when the library loads).  The call
  * allocates nothing, does not synchronise and issues no memset, so it can be
  * captured into a HIP graph (with a workspace cleared beforehand).
  * NaN or Inf inside the attended positions propagate to the output.
@@ -266,22 +267,6 @@ gqa_status gqa_decode_layer(const void *x, const void *w_qkv_packed, const void 
  */
 gqa_status gqa_meanpool_kv(const float *w, int d_model, int H, int G, int h, float *w_out, hipStream_t stream);
 
-/*
- * Measurement utility (not part of the decode path): reads `bytes` of `buf`
- * once with 16-byte loads, non-temporal if `nontemporal` is nonzero - the
- * loads of the decode kernels' cache stream - on `grid` workgroups of 256
- * threads (0: 2048), each thread taking pieces grid-stride.  The practical
- * read ceiling of the GPU, against which the decode kernels' rates are put.
- * Every thread folds its pieces with xor and writes the fold to sink[0] only
- * if it equals 0x12345678, so no read can be skipped and sink is normally
- * left untouched.
- *   buf   device, 16-byte aligned; bytes a multiple of 16 (GQA_ERR_ALIGN).
- *   sink  device, one unsigned; grid in 0..2^20 (GQA_ERR_SHAPE otherwise).
- * bytes = 0 is a no-op.  Enqueued on `stream`.
- */
-gqa_status gqa_stream_read(const void *buf, size_t bytes, int nontemporal, int grid, unsigned *sink,
-                           hipStream_t stream);
-
 /* Static description of a status code. */
 const char *gqa_status_string(gqa_status status);
 
@@ -291,8 +276,8 @@ const char *gqa_last_hip_error(void);
 /*
  * Which decode kernel a shape runs on: 0 = VALU kernel (binary32 or bfloat16
  * dot products on the vector ALUs), 1 = MFMA kernel (bfloat16 matrix cores).
- * Returns -1 for arguments gqa_decode would reject.  Selection can be forced
- * with the environment variable GQA_KERNEL=valu|mfma (bfloat16 only for mfma).
+ * Returns -1 for arguments gqa_decode would reject.  (The tuning override
+ * GQA_KERNEL=valu|mfma of gqa_measure.h forces a kernel; bfloat16 only for mfma.)
  */
 int gqa_decode_kernel_kind(int B, int H, int G, int d, int Lmax, gqa_dtype dtype);
 

@@ -15,6 +15,34 @@ def pytest_configure(config):
 import pytest  # noqa: E402
 
 
+def _reload_tuning():
+    import grouped_query_kv_decode_amd as gqa
+    if os.path.exists(gqa.library_path()):
+        gqa.tuning_reload()
+
+
+@pytest.fixture(autouse=True)
+def _tuning_follows_env(monkeypatch):
+    """The library reads its GQA_* launch-plan overrides when it loads and on
+    gqa_tuning_reload(), never during a call.  Tests set them with
+    monkeypatch.setenv / delenv; here each of those is followed by a reload,
+    and after the test the environment is restored and read once more."""
+    set_env, del_env = monkeypatch.setenv, monkeypatch.delenv
+
+    def setenv(name, value, prepend=None):
+        set_env(name, value, prepend)
+        _reload_tuning()
+
+    def delenv(name, raising=True):
+        del_env(name, raising)
+        _reload_tuning()
+
+    monkeypatch.setenv, monkeypatch.delenv = setenv, delenv
+    yield
+    monkeypatch.undo()
+    _reload_tuning()
+
+
 @pytest.fixture(autouse=True)
 def _counters_zero_between_calls(request):
     """After every GPU test: each workspace the binding cached still holds
