@@ -7,6 +7,7 @@ fallback path.  PyTorch supplies device memory and the stream.
 
 Entry points (same names as the C ABI, without the ``gqa_`` prefix):
     decode(q, k_cache, v_cache, seq_lens, scale, out=None, workspace=None)
+    decode_noalloc(q, k_cache, v_cache, seq_lens, scale, out=None)   no workspace (library scratch)
     decode_workspace_size(B, H, G, d, Lmax, dtype)
     decode_phase(phase, ...)           (split kernel / merge kernel separately)
     decode_window(q, k_cache, v_cache, seq_lens, scale, window, ...)
@@ -27,7 +28,7 @@ import ctypes
 import os
 
 __all__ = [
-    "GQAError", "decode", "decode_phase", "decode_window", "decode_append", "decode_workspace_size", "workspace_init", "meanpool_kv",
+    "GQAError", "decode", "decode_noalloc", "decode_phase", "decode_window", "decode_append", "decode_workspace_size", "workspace_init", "meanpool_kv",
     "linear", "linear_workspace_size", "pack_weight", "linear_packed", "decode_layer", "decode_layer_workspace_size", "LayerStep",
     "decode_kernel_kind", "stream_read", "tuning_reload", "status_string", "library_path", "load_library", "Decoder",
     "GQA_F32", "GQA_BF16",
@@ -37,12 +38,14 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libgqa.so")
 
 GQA_F32, GQA_BF16 = 0, 1
+NOALLOC_SCRATCH_BYTES = 32 << 20  # GQA_NOALLOC_SCRATCH_BYTES of gqa.h: the scratch of decode_noalloc
 STATUS_NAMES = {
     0: "GQA_OK", 1: "GQA_ERR_NULL", 2: "GQA_ERR_SHAPE", 3: "GQA_ERR_UNSUPPORTED", 4: "GQA_ERR_ALIGN",
     5: "GQA_ERR_WORKSPACE", 6: "GQA_ERR_SCALE", 7: "GQA_ERR_HIP", 8: "GQA_ERR_SIZE",
 }
 EXPORTED = [
-    "gqa_decode_workspace_size", "gqa_workspace_init", "gqa_decode", "gqa_decode_phase", "gqa_decode_window",
+    "gqa_decode_workspace_size", "gqa_workspace_init", "gqa_decode", "gqa_decode_noalloc", "gqa_decode_phase",
+    "gqa_decode_window",
     "gqa_decode_append", "gqa_linear_workspace_size", "gqa_linear", "gqa_pack_weight", "gqa_linear_packed",
     "gqa_decode_layer_workspace_size",
     "gqa_decode_layer", "gqa_meanpool_kv",
@@ -83,6 +86,8 @@ def load_library(path: str | None = None):
     lib.gqa_decode_phase.argtypes = [ci, vp, vp, vp, vp, ci, ci, ci, ci, ci, ctypes.c_float, ci, vp, vp, sz, vp]
     lib.gqa_decode.restype = ci
     lib.gqa_decode.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, ci, ctypes.c_float, ci, vp, vp, sz, vp]
+    lib.gqa_decode_noalloc.restype = ci
+    lib.gqa_decode_noalloc.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, ci, ctypes.c_float, ci, vp, vp]
     lib.gqa_decode_window.restype = ci
     lib.gqa_decode_window.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ctypes.c_float, ci, vp, vp, sz, vp]
     lib.gqa_decode_append.restype = ci
@@ -175,7 +180,7 @@ def _workspace_for(nbytes: int, device):
     return ws
 
 
-def _prepare(q, k_cache, v_cache, seq_lens, scale, out, workspace, window=0):
+def _prepare(q, k_cache, v_cache, seq_lens, scale, out, workspace, window=0, no_workspace=False):
     """Checks the tensors and returns (ctypes argument tuple without the stream, out, workspace)."""
     import torch
     B, H, d = q.shape
@@ -196,7 +201,7 @@ def _prepare(q, k_cache, v_cache, seq_lens, scale, out, workspace, window=0):
         out = torch.empty((B, H, d), dtype=q.dtype, device=q.device)
     elif tuple(out.shape) != (B, H, d) or out.dtype != q.dtype or not out.is_contiguous() or out.device != q.device:
         raise ValueError("out must be a contiguous [B,H,d] tensor of q's dtype on q's GPU")
-    need = decode_workspace_size(B, H, G, d, min(Lmax, window) if window > 0 else Lmax, code)
+    need = 0 if no_workspace else decode_workspace_size(B, H, G, d, min(Lmax, window) if window > 0 else Lmax, code)
     if workspace is None and need > 0:
         workspace = _workspace_for(need, q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
@@ -217,6 +222,20 @@ def decode(q, k_cache, v_cache, seq_lens, scale: float, out=None, workspace=None
     st = load_library().gqa_decode(*args, _stream_handle(q.device))
     if st:
         raise GQAError(st, "gqa_decode")
+    return out
+
+
+def decode_noalloc(q, k_cache, v_cache, seq_lens, scale: float, out=None):
+    """decode() without a workspace: the library's per-device scratch holds the
+    split partials (gqa_decode_noalloc; for callers that cannot allocate).
+    Calls on one GPU must not overlap in time."""
+    import torch
+    if out is None:
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    args, out, _ = _prepare(q, k_cache, v_cache, seq_lens, scale, out, None, no_workspace=True)
+    st = load_library().gqa_decode_noalloc(*args[:12], _stream_handle(q.device))
+    if st:
+        raise GQAError(st, "gqa_decode_noalloc")
     return out
 
 

@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 #include <string>
 
 #include "gqa.h"
@@ -686,6 +687,71 @@ gqa_status gqa_decode(const void *q, const void *k_cache, const void *v_cache, c
                       size_t workspace_bytes, hipStream_t stream) {
   return decode_impl(0, q, nullptr, nullptr, k_cache, v_cache, seq_lens, B, H, G, d, Lmax, 0, scale, dtype, out,
                      workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// The no-allocation entry point's scratch: split partials, arrival counters
+// and dispatch order of gqa_decode_noalloc, one copy on every GPU the library
+// runs on, held until the process ends.  Host code never passes this name to
+// a kernel (on the host it is only a stand-in for the device copy): each
+// device's address comes from hipGetSymbolAddress, taken once with that
+// device current.
+static __device__ __align__(256) unsigned char scratch[GQA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxScratchDevices];  // device address of `scratch`, per device (null: not set up)
+
+// The scratch of the device that `stream` belongs to; on the first call on
+// that device the address is looked up and the counter region cleared by a
+// fill kernel enqueued on `stream` (ordered before the decode that follows;
+// the kernels leave the counters zero again after every call).
+gqa_status scratch_for(hipStream_t stream, void **ptr) {
+  int dev = -1;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= kMaxScratchDevices) return GQA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = -1;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_fail(e);
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return hip_fail(e);
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    const hipError_t e2 = cur != dev ? hipSetDevice(cur) : hipSuccess;
+    if (e != hipSuccess) return hip_fail(e);
+    if (e2 != hipSuccess) return hip_fail(e2);
+    if (!p || !aligned(p, 256)) return GQA_ERR_ALIGN;
+    e = gqa::launch_fill_zero(p, kCounterBytes, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return GQA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gqa_status gqa_decode_noalloc(const void *q, const void *k_cache, const void *v_cache, const int32_t *seq_lens,
+                              int B, int H, int G, int d, int Lmax, float scale, gqa_dtype dtype, void *out,
+                              hipStream_t stream) {
+  gqa_status st = check_shape(B, H, G, d, Lmax, dtype);
+  if (st != GQA_OK) return st;
+  if (B == 0) return GQA_OK;
+  Plan pl;
+  st = get_plan(B, H, G, d, Lmax, dtype, &pl);
+  if (st != GQA_OK) return st;
+  if (pl.ws_bytes > GQA_NOALLOC_SCRATCH_BYTES) return GQA_ERR_WORKSPACE;
+  void *ws = nullptr;
+  if (pl.ws_bytes > 0 && (st = scratch_for(stream, &ws)) != GQA_OK) return st;
+  return decode_impl(0, q, nullptr, nullptr, k_cache, v_cache, seq_lens, B, H, G, d, Lmax, 0, scale, dtype, out, ws,
+                     ws ? (size_t)GQA_NOALLOC_SCRATCH_BYTES : 0, stream);
 }
 
 gqa_status gqa_decode_window(const void *q, const void *k_cache, const void *v_cache, const int32_t *seq_lens,

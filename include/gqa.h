@@ -133,6 +133,29 @@ gqa_status gqa_decode_phase(int phase, const void *q, const void *k_cache, const
                             gqa_dtype dtype, void *out, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * gqa_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): no
+ * workspace argument.  The split partials, arrival counters and dispatch
+ * order live in a scratch array of GQA_NOALLOC_SCRATCH_BYTES inside the
+ * library, one per GPU, which each GPU the library runs on holds until the
+ * process ends.  The plan, the kernels and so the results are those of
+ * gqa_decode with a workspace.
+ *   Returns GQA_ERR_WORKSPACE when the shape's plan needs more than the
+ *   scratch holds (gqa_decode_workspace_size(...) > GQA_NOALLOC_SCRATCH_BYTES);
+ *   other arguments and status codes as for gqa_decode.
+ *   The first call on a device looks the scratch up (with that device made
+ *   current for the lookup) and enqueues a fill kernel on `stream` that clears
+ *   its counters; every completed call leaves them zero again.
+ *   All calls on one GPU share its scratch: calls that overlap in time on one
+ *   GPU (on different streams or from several threads) race and give wrong
+ *   results; order them on one stream.  The call allocates and frees nothing.
+ */
+#define GQA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+gqa_status gqa_decode_noalloc(const void *q, const void *k_cache, const void *v_cache, const int32_t *seq_lens,
+                              int B, int H, int G, int d, int Lmax, float scale, gqa_dtype dtype, void *out,
+                              hipStream_t stream);
+
+/*
  * Sliding-window decode: as gqa_decode, but sequence b attends only its last
  * `window` cached positions, [max(0, len_b - window), len_b).  The wikillm
  * page "Grouped-query attention (GQA)" (Variants, decoder-only models) notes

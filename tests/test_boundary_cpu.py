@@ -190,6 +190,20 @@ def test_split_plan_model(lib, monkeypatch):
     assert lib.gqa_decode_workspace_size(128, 32, 1, 128, 1024, BF16) == 0  # 2 head chunks, one split each
 
 
+def test_noalloc_limit(lib):
+    """gqa_decode_noalloc: the binding's limit is the header's, and a shape
+    whose plan needs more scratch than that is rejected on the host (before
+    any HIP call, so this runs without a GPU) with GQA_ERR_WORKSPACE."""
+    m = re.search(r"#define GQA_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", open(HEADERS[0]).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == gqa.NOALLOC_SCRATCH_BYTES
+    big = (64, 64, 8, 128, 131072)
+    assert lib.gqa_decode_workspace_size(*big, BF16) > gqa.NOALLOC_SCRATCH_BYTES
+    args = (P, P, P, P, *big, 0.088, BF16, P, None)
+    assert lib.gqa_decode_noalloc(*args) == WS
+    assert lib.gqa_decode_noalloc(P, P, P, P, 2, 6, 4, 128, 512, 0.088, BF16, P, None) == SHAPE
+    assert lib.gqa_decode_noalloc(None, None, None, None, 0, 8, 2, 128, 512, 0.088, BF16, None, None) == OK
+
+
 def test_plan_reads_the_environment_only_on_reload(lib, monkeypatch):
     """A call never reads the GQA_* overrides: changing the environment
     without gqa_tuning_reload() leaves the plan (and so the workspace size)
