@@ -21,6 +21,8 @@ Other modes (used to produce the files under profiles/):
                                the FETCH_SIZE / WRITE_SIZE counters
     --read-ceiling             the streaming-read probe: what a kernel that only
                                reads (16-byte loads) gets from HBM
+    --timeline                 per-phase timeline of matrix-core decode calls
+                               (an instrumented build of the kernel)
     --summarize-rocprof DIR    print a summary of rocprofv3 CSV output
 """
 from __future__ import annotations
@@ -90,13 +92,45 @@ def load_traffic(workload_name: str):
     return t.get("bytes_per_dispatch")
 
 
+# The pages' only timing figures: T5-XXL inference time per sample (whole
+# encoder-decoder model, averaged over the paper's tasks, on hardware the
+# pages do not name) - context for the decode rates, not a target
+# (wikillm "Grouped-query attention (GQA)", When to use which; elemedex
+# glossary "grouped-query attention", paragraph "Grouped (GQA)").
+PAGES_T5XXL_SECONDS_PER_SAMPLE = {"MHA": 1.51, "GQA-8": 0.28, "MQA": 0.24}
+
+
+def host_threads():
+    """(threads, affinity cores, reason): the oracle takes every core of this
+    process's affinity mask, or OMP_NUM_THREADS when the launcher sets it
+    lower (a GPU host's per-GPU share of its cores)."""
+    aff = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    cap = int(omp) if omp.isdigit() and int(omp) > 0 else 0
+    if cap and cap < aff:
+        return cap, aff, "OMP_NUM_THREADS=%d, the host's share of its %d affinity cores for this GPU" % (cap, aff)
+    return aff, aff, "every core of the affinity mask"
+
+
+def versions():
+    import torch
+    rocm = None
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            rocm = f.read().strip()
+    except OSError:
+        pass
+    return {"torch": torch.__version__, "hip_runtime": torch.version.hip, "rocm": rocm,
+            "python": sys.version.split()[0]}
+
+
 def cpu_baseline(w, q, k, v, lens, out_gpu, budget_s: float):
     """Times the oracle on the host cores over whole batches of the workload."""
     import numpy as np
     import torch
     sys.path.insert(0, ROOT)
     import oracle
-    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    threads, aff, why = host_threads()
     # host copies of the attended part of the cache, one sequence at a time
     t_copy = time.perf_counter()
     seqs = []
@@ -114,7 +148,7 @@ def cpu_baseline(w, q, k, v, lens, out_gpu, budget_s: float):
         reps += 1
         if ref is None:
             ref = np.stack(outs)
-        if elapsed >= budget_s or reps >= 1000:
+        if elapsed >= budget_s or reps >= 100000:
             break
     # single-thread reference: one sequence of the batch, scaled to the batch
     qq, kk, vv, ll = seqs[0]
@@ -128,7 +162,9 @@ def cpu_baseline(w, q, k, v, lens, out_gpu, budget_s: float):
         "value": w.B * reps / elapsed, "unit": "tokens/s", "cores": threads, "kind": "oracle",
         "sample": "%d full batch(es) of the workload (%d sequences each), binary64 C oracle, %d threads over "
                   "(sequence, head); host copy %.2f s excluded" % (reps, w.B, threads, t_copy),
+        "threads_reason": why, "affinity_cores": aff, "host_cpu_count": os.cpu_count(),
         "seconds_per_batch": elapsed / reps,
+        # one sequence on one thread, scaled to the batch (uniform lengths only)
         "single_thread_seconds_per_batch": t_one * w.B if not w.ragged else None,
     }
     parity = {"max_abs_err": err, "tol": tol, "pass": bool(err <= tol and np.isfinite(got).all())}
@@ -140,7 +176,14 @@ def run_bench(args):
     import grouped_query_kv_decode_amd as gqa
     from grouped_query_kv_decode_amd import workloads as wl
 
-    w = wl.WORKLOADS[args.workload]
+    if args.shape:
+        # an unnamed shape (kernel comparisons, plan checks): full-length
+        # caches, N(0,1) values, seed 5
+        B, H, G, d, L = (int(x) for x in args.shape.split(","))
+        dt = args.dtype or "bf16"
+        w = wl.Workload("shape_%s_B%d_H%d_G%d_d%d_L%d" % (dt, B, H, G, d, L), B, H, G, d, L, dt, 5)
+    else:
+        w = wl.WORKLOADS[args.workload]
     if args.dtype == "f32" and args.variant == "layer":
         raise SystemExit("--variant layer runs the bf16 projections: use --dtype bf16")
     if args.dtype and args.dtype != w.dtype:
@@ -244,6 +287,16 @@ def run_bench(args):
         "timing": "hip_graph" if graph is not None else "eager",
         "kernels_per_step": kernels_per_step,
         "hbm_gbps_wall": ab / (ms_per_step * 1e-3) / 1e9,
+        # counter traffic (FETCH_SIZE + WRITE_SIZE per dispatch, scaled by a
+        # plain copy's counts) over the kernel time, and against the
+        # algorithmic bytes; null when the counters predate the kernel sources
+        "fetch_GBps": traffic / (avg_kernel_ms * 1e-3) / 1e9 if traffic else None,
+        "over_fetch_ratio": traffic / ab if traffic else None,
+        "seed": w.seed,
+        "versions": versions(),
+        "context": {"pages_t5xxl_seconds_per_sample": PAGES_T5XXL_SECONDS_PER_SAMPLE,
+                    "note": "whole-model T5-XXL inference time per sample on unnamed hardware (the pages' only "
+                            "timings); not comparable with one attention layer's decode call"},
     }
     if not args.no_cpu_baseline and args.variant == "decode":
         q, k, v, lens = sets[0]
@@ -496,7 +549,7 @@ def write_traffic(args):
         "copy_fetch_factor": f_fac, "copy_write_factor": w_fac,
         "bytes_per_dispatch": (fetch / f_fac + write / w_fac) * 1024.0,
     }
-    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % args.workload)
+    path = os.path.join(args.traffic_dir or os.path.join(ROOT, "profiles"), "traffic_%s.json" % args.workload)
     with open(path, "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec))
@@ -563,12 +616,27 @@ def summarize_rocprof(d):
     return "\n".join(out)
 
 
+# the per-phase timeline: the bench default, the small calls, and the largest T5-XXL
+# point that needs no split (workload, window)
+TIMELINE_CASES = [("mistral7b_bf16_B16_H32_G8_d128_L4096", 0), ("t5xxl_bf16_B32_H64_G1_d64_L2048", 0),
+                  ("t5xxl_bf16_B32_H64_G4_d64_L2048", 0), ("t5xxl_bf16_B32_H64_G8_d64_L2048", 0),
+                  ("mistral7b_bf16_B16_H32_G8_d128_L4096", 1024)]
+
+ALL_WORKLOADS = ["tiny_f32_B1_H8_G2_d64_L256", "mistral7b_bf16_B16_H32_G8_d128_L4096",
+                 "t5xxl_bf16_B32_H64_G1_d64_L2048", "t5xxl_bf16_B32_H64_G4_d64_L2048",
+                 "t5xxl_bf16_B32_H64_G8_d64_L2048", "t5xxl_bf16_B32_H64_G16_d64_L2048",
+                 "t5xxl_bf16_B32_H64_G64_d64_L2048", "gemma2_27b_bf16_B8_H32_G16_d128_L8192",
+                 "ragged_bf16_B64_H64_G8_d128_Lmax32768"]
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="mistral7b_bf16_B16_H32_G8_d128_L4096")
+    ap.add_argument("--workload", default="mistral7b_bf16_B16_H32_G8_d128_L4096",
+                    help="a named workload, or 'all' (one JSON line per named workload)")
+    ap.add_argument("--shape", metavar="B,H,G,d,L", help="an unnamed full-length shape instead of a workload")
     ap.add_argument("--rotate", type=int, default=0, help="input sets cycled through (default: >= 1 GiB of caches)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--dtype", choices=["bf16", "f32"], default=None,
@@ -582,6 +650,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time to aim for")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--read-ceiling", action="store_true", help="the streaming-read probe (read ceiling of HBM)")
+    ap.add_argument("--timeline", action="store_true",
+                    help="per-phase timeline of matrix-core decode calls (needs libgqa_timeline.so: "
+                         "python -m grouped_query_kv_decode_amd.timeline build)")
     ap.add_argument("--meanpool", action="store_true", help="time the K/V mean-pool conversion step")
     ap.add_argument("--fig6", action="store_true", help="the pages' fig. 6 group sweep as decoder attention")
     ap.add_argument("--fig6-batch", type=int, default=32)
@@ -593,6 +664,7 @@ def main():
     ap.add_argument("--write-dir")
     ap.add_argument("--copy-fetch-dir")
     ap.add_argument("--copy-write-dir")
+    ap.add_argument("--traffic-dir", help="where --write-traffic puts traffic_<workload>.json (default profiles/)")
     args = ap.parse_args()
     if args.summarize_rocprof:
         print(summarize_rocprof(args.summarize_rocprof))
@@ -614,11 +686,26 @@ def main():
     if args.read_ceiling:
         read_ceiling(args)
         return 0
+    if args.timeline:
+        from grouped_query_kv_decode_amd import timeline
+        timeline.run(TIMELINE_CASES)
+        return 0
     if args.fig6:
         fig6(args)
         return 0
     if args.shapes:
         shapes_bench(args)
+        return 0
+    if args.workload == "all":
+        # every named workload, one JSON line each (the T5-XXL shape at every group count)
+        import gc
+        import torch
+        from grouped_query_kv_decode_amd import workloads as wl
+        for name in ALL_WORKLOADS:
+            args.workload = name
+            run_bench(args)
+            gc.collect()
+            torch.cuda.empty_cache()
         return 0
     run_bench(args)
     return 0

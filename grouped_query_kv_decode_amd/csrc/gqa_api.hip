@@ -55,6 +55,7 @@ struct Tuning {
   int merge_kernel;  // GQA_MERGE=kernel
   int order;         // GQA_ORDER=0|1 (-1: the plan's)
   int valu_pieces;   // GQA_VALU_PIECES=1: one 16-byte piece per lane and row
+  int arrive_acqrel; // GQA_ARRIVE=acqrel: release/acquire ordering on the arrival counter
   int linear_waves, linear_ksplit, linear_tpi, linear_strips;  // GQA_LINEAR_*
   int linear_unroll;                                           // GQA_LINEAR_UNROLL=0: 0, else -1
 };
@@ -75,6 +76,7 @@ Tuning read_tuning() {
   t.order = env_is("GQA_ORDER", "0") ? 0 : (env_is("GQA_ORDER", "1") ? 1 : -1);
   const char *pieces = getenv("GQA_VALU_PIECES");
   t.valu_pieces = pieces && pieces[0] == '1';
+  t.arrive_acqrel = env_is("GQA_ARRIVE", "acqrel");
   t.linear_waves = env_int("GQA_LINEAR_WAVES", 0);
   t.linear_ksplit = env_int("GQA_LINEAR_KSPLIT", 0);
   t.linear_tpi = env_int("GQA_LINEAR_TPI", 0);
@@ -120,6 +122,7 @@ struct Plan {
   int nontemporal;  // matrix-core cache loads non-temporal (plain when head chunks share lines)
   int contig;       // matrix-core tiles as contiguous per-wave runs (tuning only)
   int valu_pieces;  // VALU kernel forced to one 16-byte piece per lane and row (tuning only)
+  int arrive_acqrel;  // release/acquire arrival counter
   unsigned grid;
   size_t ml_off, o_off, order_off, ws_bytes;
 };
@@ -132,9 +135,10 @@ gqa_status check_shape(int B, int H, int G, int d, int Lmax, gqa_dtype dt) {
 }
 
 // Decode launch plan (tuned on MI355X with the workload sweep):
-//  - kernel: bfloat16 uses the matrix-core kernel for r = H/G in 2..64 and
-//    the VALU kernel for r = 1, where it measured faster (no 16-head padding);
-//    fp32 always uses the VALU kernel.  GQA_KERNEL=valu|mfma overrides.
+//  - kernel: bfloat16 uses the matrix-core kernel for r = H/G in 2..64, and
+//    for r = 1 on calls that stream at least 32 MiB of K and V (smaller MHA
+//    calls take the VALU kernel, whose one-round plan splits less); fp32
+//    always uses the VALU kernel.  GQA_KERNEL=valu|mfma overrides.
 //  - workgroups of the matrix-core kernel have 4 waves (GQA_WAVES = 8 or 16
 //    overrides where the register budget for the head blocks allows).
 //  - with fewer (b, g) units than compute units the matrix-core kernel
@@ -164,7 +168,18 @@ gqa_status check_shape(int B, int H, int G, int d, int Lmax, gqa_dtype dt) {
 //    small kernel sorts from the lengths on the device (GQA_ORDER=0/1).
 gqa_status make_plan(int B, int H, int G, int d, int Lmax, gqa_dtype dt, const Tuning &tu, Plan *pl) {
   const int r = H / G;
-  int kind = (dt == GQA_BF16 && r >= 2 && r <= 64) ? KIND_MFMA : KIND_VALU;
+  // bfloat16 runs on the matrix cores for r = 2..64, and for r = 1 (MHA)
+  // once the call streams at least 32 MiB of K and V: rocprofv3 / graph-
+  // replay times, matrix cores against VALU, B8 H32 G32 d128 L8192 150.8 /
+  // 158.9 us, B4 H16 G16 d128 L32768 153.0 / 161.9, B64 H8 G8 d128 L4096
+  // 153.0 / 157.3, B32 H64 G64 d64 L2048 156.1 / 157.6, B8 H16 G16 d64
+  // L2048 (67 MB) 14.8 / 16.1, B2 H8 G8 d128 L4096 (33.5 MB) 12.7 / 13.5;
+  // below, the VALU kernel's one-round plan (fewer splits) wins: B4 H32 G32
+  // d64 L512 (16.8 MB) 7.61 / 7.30 us, B1 H16 G16 d128 L1024 (8.4 MB)
+  // 8.71 / 8.07 us.
+  const double kv_bytes = 4.0 * B * G * (double)Lmax * d;
+  const bool mha_on_mfma = r == 1 && kv_bytes >= 32.0 * 1024 * 1024;
+  int kind = (dt == GQA_BF16 && ((r >= 2 && r <= 64) || mha_on_mfma)) ? KIND_MFMA : KIND_VALU;
   if (tu.kernel == 1 + KIND_VALU) kind = KIND_VALU;
   if (tu.kernel == 1 + KIND_MFMA && dt == GQA_BF16 && r <= 64) kind = KIND_MFMA;
   pl->kind = kind;
@@ -363,6 +378,7 @@ gqa_status make_plan(int B, int H, int G, int d, int Lmax, gqa_dtype dt, const T
   pl->nontemporal = tu.temporal >= 0 ? !tu.temporal : pl->HC == 1 || kind != KIND_MFMA;
   pl->contig = tu.contig;
   pl->valu_pieces = tu.valu_pieces;
+  pl->arrive_acqrel = tu.arrive_acqrel;
   if (pl->S > 1) {
     pl->ml_off = kCounterBytes;
     pl->o_off = pl->ml_off + round_up((size_t)B * H * pl->S * sizeof(float2), 256);
@@ -639,6 +655,7 @@ gqa_status decode_impl(int phase, const void *q, const void *k_new, const void *
   p.order = order;
   p.fused = pl.fused;
   p.contig = pl.contig;
+  p.arrive_acqrel = pl.arrive_acqrel;
   p.B = B;
   p.H = H;
   p.G = G;

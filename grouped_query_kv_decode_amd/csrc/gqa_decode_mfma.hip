@@ -433,7 +433,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma(DecodeParams p) {
     }
   }
   if (nsplit == 1 || !p.fused) return;
-  if (!arrive_last(p.ws_cnt + ((size_t)b * p.G + g) * p.HC + hc, nsplit)) return;
+  if (!arrive_last(p.ws_cnt + ((size_t)b * p.G + g) * p.HC + hc, nsplit, p.arrive_acqrel)) return;
   merge_heads<__bf16, D>(p, b, head0, rw, nsplit);
 }
 

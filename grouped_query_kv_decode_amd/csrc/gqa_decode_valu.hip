@@ -345,7 +345,7 @@ __global__ __launch_bounds__(256) void decode_valu(DecodeParams p) {
     }
   }
   if (nsplit == 1 || !p.fused) return;
-  if (!arrive_last(p.ws_cnt + ((size_t)b * p.G + g) * p.HC + hc, nsplit)) return;
+  if (!arrive_last(p.ws_cnt + ((size_t)b * p.G + g) * p.HC + hc, nsplit, p.arrive_acqrel)) return;
   merge_heads<T, D>(p, b, head0, nh, nsplit);
 }
 

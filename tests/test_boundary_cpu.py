@@ -246,12 +246,15 @@ def test_kernel_selection(lib, monkeypatch):
     assert lib.gqa_decode_kernel_kind(16, 32, 8, 128, 4096, BF16) == 1
     assert lib.gqa_decode_kernel_kind(1, 8, 2, 64, 256, F32) == 0
     assert lib.gqa_decode_kernel_kind(1, 128, 1, 64, 256, BF16) == 0  # more than 64 heads per group
-    assert lib.gqa_decode_kernel_kind(32, 64, 64, 64, 2048, BF16) == 0  # r = 1: VALU measured faster
+    assert lib.gqa_decode_kernel_kind(32, 64, 64, 64, 2048, BF16) == 1  # r = 1, 1 GiB of K and V: matrix cores
+    assert lib.gqa_decode_kernel_kind(2, 8, 8, 128, 4096, BF16) == 1    # r = 1, 32 MiB
+    assert lib.gqa_decode_kernel_kind(4, 32, 32, 64, 512, BF16) == 0    # r = 1, 16 MiB: the VALU kernel
+    assert lib.gqa_decode_kernel_kind(2, 8, 8, 128, 4095, BF16) == 0    # just under 32 MiB
     assert lib.gqa_decode_kernel_kind(1, 6, 4, 64, 256, BF16) == -1
     monkeypatch.setenv("GQA_KERNEL", "valu")
     assert lib.gqa_decode_kernel_kind(16, 32, 8, 128, 4096, BF16) == 0
     monkeypatch.setenv("GQA_KERNEL", "mfma")
-    assert lib.gqa_decode_kernel_kind(32, 64, 64, 64, 2048, BF16) == 1
+    assert lib.gqa_decode_kernel_kind(4, 32, 32, 64, 512, BF16) == 1
     assert lib.gqa_decode_kernel_kind(1, 8, 2, 64, 256, F32) == 0  # no fp32 matrix-core path
 
 

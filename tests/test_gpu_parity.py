@@ -444,11 +444,44 @@ def test_equal_queries_in_a_group(env):
         assert torch.equal(out[0, h], out[0, 4])
 
 
+MHA_CASES = [(3, 8, 8, 128, 3000, [3000, 1, 1777]), (2, 16, 16, 64, 2100, [2100, 33])]
+
+
+@pytest.mark.parametrize("case", MHA_CASES, ids=["d128", "d64"])
+@pytest.mark.parametrize("plan", [(None, None), (256, None), (256, "kernel"), (100000, None)],
+                         ids=["default_split", "split256", "split256_mergekernel", "unsplit"])
+def test_mha_on_matrix_cores(env, case, plan):
+    """r = 1 (G = H) on the matrix-core kernel, the default for bfloat16 MHA
+    calls of at least 32 MiB of K and V (forced here on small shapes): one
+    real head in a block of 16.  Plain decode, sliding window and the cache
+    append against the oracle."""
+    chunk, merge = plan
+    env(GQA_KERNEL="mfma", GQA_CHUNK=chunk, GQA_MERGE=merge)
+    B, H, G, d, L, lens = case
+    assert gqa.decode_kernel_kind(B, H, G, d, L, gqa.GQA_BF16) == 1
+    q, k, v, lt, scale = rand_case(B, H, G, d, L, lens, "bf16", seed=700 + d)
+    check(run_gpu(q, k, v, lt, scale), oracle_out(q, k, v, lt, scale), "bf16", "MHA mfma %s %s" % (plan, case[:5]))
+    out_w = gqa.decode_window(q, k, v, lt, scale, 1000)
+    torch.cuda.synchronize()
+    check(out_w, oracle.decode(q.cpu(), k.cpu(), v.cpu(), lt.cpu(), scale, window=1000), "bf16", "MHA mfma window")
+    gen = torch.Generator(DEV).manual_seed(701)
+    kn = torch.randn((B, G, d), generator=gen, device=DEV).to(torch.bfloat16)
+    vn = torch.randn((B, G, d), generator=gen, device=DEV).to(torch.bfloat16)
+    k0, v0 = k.cpu(), v.cpu()
+    out_a = gqa.decode_append(q, kn, vn, k, v, lt, scale)
+    torch.cuda.synchronize()
+    ref, rk, rv = oracle.decode_append(q.cpu(), kn.cpu(), vn.cpu(), k0, v0, lt.cpu(), scale)
+    check(out_a, ref, "bf16", "MHA mfma append")
+    assert np.array_equal(k.cpu().view(torch.int16).numpy().view(np.uint16), rk.view(np.uint16))
+    assert np.array_equal(v.cpu().view(torch.int16).numpy().view(np.uint16), rv.view(np.uint16))
+
+
 # Invariants of the decode-step block (softmax weights, then their weighted
 # sum of value rows) on every kernel and merge path: unsplit, split with the
 # in-kernel merge, split with the merge kernel; both element types.
 INVARIANT_PLANS = [("default", 100000, None), ("default", 128, None), ("default", 128, "kernel"),
-                   ("valu", 100000, None), ("valu", 128, None), ("valu", 128, "kernel")]
+                   ("valu", 100000, None), ("valu", 128, None), ("valu", 128, "kernel"),
+                   ("mfma", 100000, None), ("mfma", 256, None)]  # (binary32 has no matrix-core path: VALU)
 INVARIANT_CASES = [(3, 32, 8, 128, 600, [600, 257, 1]),   # r = 4
                    (2, 64, 4, 64, 500, [500, 33]),        # r = 16
                    (2, 8, 8, 128, 300, [300, 129])]       # r = 1
