@@ -75,3 +75,26 @@ def test_noalloc_binding_and_repeat():
     torch.cuda.synchronize()
     for o in outs:
         assert torch.equal(o, ref)
+
+
+def test_noalloc_graph_replays():
+    """The callers it is for capture it: after one eager call on the device
+    (which sets the scratch up), gqa_decode_noalloc captured into a HIP graph
+    and replayed five times with new queries written between replays, every
+    replay bit-equal to gqa_decode with a workspace on the same inputs."""
+    lib = gqa.load_library()
+    w, q, k, v, lt = _case(4, 32, 8, 128, 3000, [3000, 2047, 1, 1500], "bf16", 6)
+    out = torch.empty_like(q)
+    _noalloc(lib, w, q, k, v, lt, out)  # set-up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        _noalloc(lib, w, q, k, v, lt, out)
+    gen = torch.Generator(DEV).manual_seed(7)
+    for rep in range(5):
+        q.copy_(torch.randn(q.shape, generator=gen, device=DEV).to(q.dtype))
+        g.replay()
+        torch.cuda.synchronize()
+        ref = gqa.decode(q, k, v, lt, w.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), rep
