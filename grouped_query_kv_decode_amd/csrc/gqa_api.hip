@@ -363,8 +363,16 @@ gqa_status make_plan(int B, int H, int G, int d, int Lmax, gqa_dtype dt, const T
   pl->grid = (unsigned)grid;
   // In-kernel merge: one counter per unit, and a merging workgroup that
   // reads every split of its heads, which pays up to kMaxFusedSplits; beyond
-  // that a merge kernel spread over heads, dimensions and splits.
-  pl->wide = pl->S > fused_max;
+  // that, or when that one workgroup would read more than 96 KiB of partials
+  // through its compute unit, a merge kernel spread over heads, dimensions
+  // and splits.  Graph replays, in-kernel / merge kernel: B3 H64 G4 d128
+  // L8192 (16 heads x 21 splits, 175 KB) 20.8 / 17.9 us, B4 H64 G4 d128
+  // L8192 (133 KB) 21.3 / 20.0 us; at 66 KB and below the in-kernel merge
+  // wins (B1 H32 G8 d128 L32768 28.1 / 27.8, B20 H8 G1 d128 L4096 54 KB
+  // 13.9 / 14.8, T5-XXL G = 1 34 KB 11.4 / 16.4, Mistral-7B shape 42.5 / 45.5).
+  const long partial_bytes = (long)(pl->kind == KIND_MFMA ? (16 * pl->HB < r ? 16 * pl->HB : r) : pl->RC) *
+                             pl->S * (d + 2) * 4;
+  pl->wide = pl->S > fused_max || (pl->S > 1 && partial_bytes > 96 * 1024);
   pl->fused = units <= kMaxFusedUnits && !pl->wide && !tu.merge_kernel;
   // Grids of several rounds with at least kOrderMinSplits splits per
   // sequence: the order kernel sorts the items largest first (ragged lengths

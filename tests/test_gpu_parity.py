@@ -179,6 +179,20 @@ def test_many_splits_window_and_append(env):
     assert np.array_equal(v.cpu().view(torch.int16).numpy().view(np.uint16), rv.view(np.uint16))
 
 
+def test_wide_merge_by_partial_bytes(env):
+    """At most 32 splits, but 16 heads x 16 splits of 128-dimension partials
+    (133 KB) for the merging workgroup to read: the plan takes the wide merge
+    kernel.  Against the oracle (full, partial and one-position sequences),
+    and the same bits call after call."""
+    B, H, G, d, L = 3, 64, 4, 128, 4096
+    lens = [4096, 2049, 1]
+    q, k, v, lt, scale = rand_case(B, H, G, d, L, lens, "bf16", seed=860)
+    out = run_gpu(q, k, v, lt, scale).clone()
+    check(out, oracle_out(q, k, v, lt, scale), "bf16", "wide merge by bytes")
+    for _ in range(3):
+        assert torch.equal(run_gpu(q, k, v, lt, scale), out)
+
+
 def test_long_single_sequence(env):
     """One sequence, one K/V head, 131072 positions: the planner's 256 splits
     of 512 positions (every compute unit busy), merged by the wide kernel."""
