@@ -40,7 +40,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, published
 METRIC = "decode tokens/sec + achieved HBM GB/s (% of peak) for GQA decode at 1 GPU"
-KERNEL_SOURCES = ["gqa_device.h", "gqa_decode_mfma.hip", "gqa_decode_valu.hip"]
+KERNEL_SOURCES = ["gqa_device.h", "gqa_decode_mfma.hip", "gqa_decode_mfma_f32.hip", "gqa_decode_valu.hip"]
 
 
 def kernel_source_hash() -> str:

@@ -34,6 +34,7 @@ SOURCES = [
     # keep MFMA accumulators in VGPRs: the softmax rescale then needs no
     # AGPR<->VGPR copies in the streaming loop
     ("gqa_decode_mfma.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]),
+    ("gqa_decode_mfma_f32.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]),
     ("gqa_decode_valu.hip", []),
     ("gqa_merge.hip", []),
     ("gqa_order.hip", []),

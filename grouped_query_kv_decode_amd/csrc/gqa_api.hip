@@ -177,11 +177,23 @@ gqa_status make_plan(int B, int H, int G, int d, int Lmax, gqa_dtype dt, const T
   // below, the VALU kernel's one-round plan (fewer splits) wins: B4 H32 G32
   // d64 L512 (16.8 MB) 7.61 / 7.30 us, B1 H16 G16 d128 L1024 (8.4 MB)
   // 8.71 / 8.07 us.
+  //
+  // binary32 runs on the matrix cores (v_mfma_f32_16x16x4_f32) for r = 3..64,
+  // a workgroup per block of 16 heads (HIP-event times, matrix cores / VALU):
+  // B16 H32 G8 d128 L4096 82.9 / 91.0 us, B32 H64 G8 d64 L2048 42.0 / 61.0,
+  // B32 H64 G4 d64 L2048 25.0 / 62.7, B8 H48 G4 d128 L4096 27.2 / 64.5,
+  // B1 H8 G2 d64 L256 6.8 / 8.8; r = 24..64: B16 H48 G2 d128 L4096 33.3 /
+  // 88.8, B8 H64 G2 d128 L4096 21.7 / 66.9, B32 H64 G1 d64 L2048 18.9 / 66.8,
+  // B4 H64 G1 d128 L8192 23.7 / 75.9.  At r = 2 and r = 1 the two are within
+  // 1% (B8 H32 G16 d128 L8192 156.9 / 156.0, B16 H16 G8 d128 L4096 82.0 /
+  // 81.8, B8 H32 G32 d128 L4096 154.8 / 153.5) and the VALU kernel stays.
   const double kv_bytes = 4.0 * B * G * (double)Lmax * d;
   const bool mha_on_mfma = r == 1 && kv_bytes >= 32.0 * 1024 * 1024;
-  int kind = (dt == GQA_BF16 && ((r >= 2 && r <= 64) || mha_on_mfma)) ? KIND_MFMA : KIND_VALU;
+  int kind = (dt == GQA_BF16 && ((r >= 2 && r <= 64) || mha_on_mfma)) || (dt == GQA_F32 && r >= 3 && r <= 64)
+                 ? KIND_MFMA
+                 : KIND_VALU;
   if (tu.kernel == 1 + KIND_VALU) kind = KIND_VALU;
-  if (tu.kernel == 1 + KIND_MFMA && dt == GQA_BF16 && r <= 64) kind = KIND_MFMA;
+  if (tu.kernel == 1 + KIND_MFMA && r <= 64) kind = KIND_MFMA;
   pl->kind = kind;
   pl->NW = 4;
   const int target = tu.target_wgs > 0 ? tu.target_wgs : 256;
@@ -200,7 +212,7 @@ gqa_status make_plan(int B, int H, int G, int d, int Lmax, gqa_dtype dt, const T
   // merged by a second kernel), at most max_chunk positions.
   auto chunk_of = [&](long S) {
     int chunk = (int)round_up((size_t)ceil_div(Lmax, S < 1 ? 1 : S), 32);
-    const int min_chunk = kind == KIND_MFMA ? 256 : 32;
+    const int min_chunk = kind == KIND_MFMA ? (dt == GQA_F32 ? 64 : 256) : 32;
     if (chunk < min_chunk) chunk = min_chunk;
     const int min_for_merge = (int)round_up((size_t)ceil_div(Lmax, kMaxSplits), 32);
     if (chunk < min_for_merge) chunk = min_for_merge;
@@ -218,7 +230,7 @@ gqa_status make_plan(int B, int H, int G, int d, int Lmax, gqa_dtype dt, const T
   auto plan_cost = [&](long units, int heads, int chunk) {
     const long S = ceil_div(Lmax, chunk);
     const long rounds = (units * S + 255) / 256;
-    double e = rounds * ((double)chunk * d * 4 / 1024 + 64.0);
+    double e = rounds * ((double)chunk * d * (dt == GQA_F32 ? 8 : 4) / 1024 + 64.0);
     if (S > 1) e += 128.0 + (S > fused_max ? 128.0 : 4.0 * heads * S * (d + 2) * 4 / 1024);
     return e;
   };
@@ -257,6 +269,39 @@ gqa_status make_plan(int B, int H, int G, int d, int Lmax, gqa_dtype dt, const T
     }
     return best;
   };
+  // Binary32 on the matrix cores, grids of one round: the split count of
+  // lowest estimated time among the target's count halved down to 1.  In us:
+  // a workgroup streams ~40 KiB of K and V per us (its 16-position tiles
+  // take one per wave, so a 64-position split is one tile per wave) and the
+  // merging one reads its unit's partials at that rate; ~1.4 us for the
+  // split protocol (partial stores, arrival), ~4 us for a separate wide
+  // merge kernel, ~0.012 us per workgroup dispatched.  Fitted to HIP-graph
+  // replays (split length: us): B1 H8 G2 d64 L256 64: 5.64, 128: 6.61,
+  // 256: 6.75; B1 H8 G2 d64 L1024 64: 6.75, 128: 7.19, 256: 8.39; B1 H32 G8
+  // d128 L512 64: 7.85, 128: 9.11, 256: 12.24; B2 H32 G8 d128 L1024 64:
+  // 11.20, 128: 10.69, 256: 13.01; B4 H32 G8 d128 L1024 128: 11.48, 256: 13.66.
+  auto f32_mfma_chunk = [&](long units, int heads, int base) {
+    auto est = [&](int chunk) {
+      const long S = ceil_div(Lmax, chunk);
+      double e = chunk * d * 8.0 / 1024 / 40 + 0.012 * units * S;
+      if (S > 1) {
+        const double part_kib = (double)heads * S * (d + 2) * 4 / 1024;
+        e += 1.4 + ((S > fused_max || part_kib > 96) ? 4.0 : part_kib / 40);
+      }
+      return e;
+    };
+    int best = base;
+    double best_e = est(base);
+    for (long S = ceil_div(Lmax, base) / 2; S >= 1; S /= 2) {
+      const int c = chunk_of(S);
+      const double e = est(c);
+      if (e < best_e) {
+        best_e = e;
+        best = c;
+      }
+    }
+    return best;
+  };
   // Split length for a grid of `units` (b, g, head chunk) units of `heads`
   // query heads each: about `target` workgroups (one per compute unit).  On
   // the matrix cores the split count is then the one of lowest plan_cost
@@ -286,6 +331,7 @@ gqa_status make_plan(int B, int H, int G, int d, int Lmax, gqa_dtype dt, const T
     const int base = chunk_of((tgt + units - 1) / units);
     if (target_env) return base;
     if (kind != KIND_MFMA) return valu_chunk(units, base);
+    if (dt == GQA_F32 && units * ceil_div(Lmax, base) <= 256) return f32_mfma_chunk(units, heads, base);
     const long s_max = ceil_div(Lmax, base) > fused_max ? ceil_div(Lmax, base) : (long)fused_max;
     auto est = [&](int chunk) { return plan_cost(units, heads, chunk); };
     int best = base;
@@ -338,6 +384,10 @@ gqa_status make_plan(int B, int H, int G, int d, int Lmax, gqa_dtype dt, const T
     if (hc_env == 1 || hc_env == 2 || hc_env == 4) hc = fit(hc_env > hb_all ? hb_all : hc_env);
     pl->HC = hc;
     pl->HB = hb_all / hc;
+    if (dt == GQA_F32) {  // the binary32 kernel serves one head block: a workgroup per block
+      pl->HC = hb;
+      pl->HB = 1;
+    }
     pl->NW = 4;  // chosen below, once the split length is known
     pl->RC = 0;
   } else {
@@ -352,7 +402,7 @@ gqa_status make_plan(int B, int H, int G, int d, int Lmax, gqa_dtype dt, const T
     // 4 waves (measured best on every workload with the non-temporal cache
     // stream); 8 or 16 on request where the head blocks fit the register
     // budget of the larger workgroup.
-    const int nw_max = (pl->HB == 1 && d == 64) ? 16 : (pl->HB <= 2 ? 8 : 4);
+    const int nw_max = dt == GQA_F32 ? 4 : (pl->HB == 1 && d == 64) ? 16 : (pl->HB <= 2 ? 8 : 4);
     const int nw_def = 4;
     const int nw = tu.waves > 0 ? tu.waves : nw_def;
     pl->NW = (nw == 8 || nw == 16) && nw <= nw_max ? nw : 4;
@@ -681,8 +731,9 @@ gqa_status decode_impl(int phase, const void *q, const void *k_new, const void *
   }
   if (phase != 2) {
     const hipError_t e =
-        pl.kind == KIND_MFMA ? gqa::launch_decode_mfma(p, d, pl.HB, pl.NW, pl.nontemporal, pl.grid, stream)
-                             : gqa::launch_decode_valu(p, (int)dtype, d, pl.RC, pl.valu_pieces, pl.grid, stream);
+        pl.kind != KIND_MFMA ? gqa::launch_decode_valu(p, (int)dtype, d, pl.RC, pl.valu_pieces, pl.grid, stream)
+        : dtype == GQA_F32   ? gqa::launch_decode_mfma_f32(p, d, pl.nontemporal, pl.grid, stream)
+                             : gqa::launch_decode_mfma(p, d, pl.HB, pl.NW, pl.nontemporal, pl.grid, stream);
     if (e != hipSuccess) return hip_fail(e);
   }
   if (phase != 1 && pl.S > 1 && !pl.fused) {

@@ -241,6 +241,8 @@ hipError_t launch_decode_valu(const DecodeParams &p, int dtype, int D, int RC, i
 // head chunks read the same lines; four head blocks always stream).
 hipError_t launch_decode_mfma(const DecodeParams &p, int D, int HB, int NW, int nontemporal, unsigned grid,
                               hipStream_t stream);
+// binary32 on the matrix cores: one head block of up to 16 heads per workgroup
+hipError_t launch_decode_mfma_f32(const DecodeParams &p, int D, int nontemporal, unsigned grid, hipStream_t stream);
 hipError_t launch_merge(const DecodeParams &p, int dtype, int D, int heads_per_unit, hipStream_t stream);
 hipError_t launch_merge_wide(const DecodeParams &p, int dtype, int D, hipStream_t stream);
 hipError_t launch_order(const DecodeParams &p, bool valu_layout, unsigned grid, int *order, hipStream_t stream);

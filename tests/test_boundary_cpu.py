@@ -126,8 +126,9 @@ def _decode_ws(B, H, S, d, grid=0):
 def test_split_plan_model(lib, monkeypatch):
     """Split lengths: about 256 workgroups (on the matrix cores the count
     that fills whole rounds of 256 best), at least 256 positions on the
-    matrix cores (32 on the VALU kernel), at least Lmax/256, at most 8192
-    on the matrix cores and 4096 on the VALU kernel."""
+    bfloat16 matrix-core kernel (64 on the binary32 one, 32 on the VALU
+    kernel), at least Lmax/256, at most 8192 on the matrix cores and 4096 on
+    the VALU kernel."""
     for k in ("GQA_CHUNK", "GQA_TARGET_WGS", "GQA_MAX_CHUNK", "GQA_KERNEL", "GQA_HEAD_SPLIT", "GQA_MERGE", "GQA_ORDER",
               "GQA_FUSED_MAX_SPLITS"):
         monkeypatch.delenv(k, raising=False)
@@ -138,21 +139,18 @@ def test_split_plan_model(lib, monkeypatch):
         (4, 32, 8, 128, 4096, BF16, 8),       # 32 units: 512
         (1, 32, 8, 128, 32768, BF16, 32),     # 8 units, long: 1024 (256 WGs)
         (64, 64, 8, 128, 32768, BF16, 4, 2048),  # 512 units: 8192 cap; 2048 workgroups, ordered
-        (64, 64, 8, 128, 32768, F32, 8, 4096),   # VALU: 4096 cap; 4096 workgroups, ordered
+        (64, 64, 8, 128, 32768, F32, 4, 2048),   # binary32 r = 8, matrix cores: 8192 cap; ordered
         (8, 32, 16, 128, 8192, BF16, 2),      # 128 units: 4096
-        # VALU grids of one round: the target's split count halved while the
-        # estimate falls (fewer splits where the merge costs more than it saves)
-        (1, 8, 2, 64, 1024, F32, 8),          # 2 units: 32 -> 8 splits of 128
-        (1, 32, 8, 128, 512, F32, 8),         # 8 units: 16 -> 8 splits of 64
+        # binary32 on the matrix cores, grids of one round: 64-position floor,
+        # the target's split count halved while the estimate falls
+        (1, 8, 2, 64, 256, F32, 4),           # 2 units: 4 splits of 64
+        (1, 8, 2, 64, 1024, F32, 16),         # 2 units: 16 splits of 64
+        (1, 32, 8, 128, 512, F32, 8),         # 8 units: 8 splits of 64
+        (2, 32, 8, 128, 1024, F32, 8),        # 16 units: 16 -> 8 splits of 128
+        (4, 32, 8, 128, 1024, F32, 8),        # 32 units: 256 workgroups
+        (1, 8, 2, 64, 8192, F32, 32),         # 2 units: 128 -> 32 splits (no wide merge)
+        (16, 32, 8, 128, 4096, F32, 2),       # 128 units: 2048
         (1, 16, 16, 128, 1024, BF16, 8),      # r = 1 (VALU), 16 units: 16 -> 8 splits of 128
-        (2, 8, 2, 128, 2048, F32, 64),        # 4 units: keeps 64 splits of 32 (wide merge)
-        # binary32, 4 heads per row set: 512 workgroups where the units divide
-        # 512, else 768; 8 heads per row set: 768
-        (4, 32, 8, 128, 8192, F32, 16),       # 32 units: 512 workgroups
-        (16, 32, 8, 128, 4096, F32, 4),       # 128 units: 512
-        (12, 32, 8, 128, 2048, F32, 8),       # 96 units do not divide 512: 768
-        (2, 64, 8, 128, 8192, F32, 43),       # 8 heads per row set: 768 aimed at, 192-position splits
-        (1, 8, 2, 64, 8192, F32, 256),        # VALU, 2 units of 4 heads: 768 workgroups aimed at, 32-position splits
         (1, 8, 1, 128, 131072, BF16, 256),    # one unit, long: 512-position splits (256 WGs)
         (1, 8, 1, 128, 262144, F32, 256),     # at most 256 splits: 1024 positions
         # 64 heads per K/V head: 2 or 4 head chunks, whichever moves fewer
@@ -178,13 +176,36 @@ def test_split_plan_model(lib, monkeypatch):
     ]
     for B, H, G, d, L, dt, S, *grid in cases:
         assert lib.gqa_decode_workspace_size(B, H, G, d, L, dt) == _decode_ws(B, H, S, d, *grid), (B, H, G, d, L, dt, S)
+    # binary32 on the VALU kernel (the default for r <= 2; forced here)
+    valu_cases = [
+        (64, 64, 8, 128, 32768, F32, 8, 4096),   # 4096 cap; 4096 workgroups, ordered
+        # grids of one round: the target's split count halved while the
+        # estimate falls (fewer splits where the merge costs more than it saves)
+        (1, 8, 2, 64, 1024, F32, 8),          # 2 units: 32 -> 8 splits of 128
+        (1, 32, 8, 128, 512, F32, 8),         # 8 units: 16 -> 8 splits of 64
+        (2, 8, 2, 128, 2048, F32, 64),        # 4 units: keeps 64 splits of 32 (wide merge)
+        # 4 heads per row set: 512 workgroups where the units divide 512,
+        # else 768; 8 heads per row set: 768
+        (4, 32, 8, 128, 8192, F32, 16),       # 32 units: 512 workgroups
+        (16, 32, 8, 128, 4096, F32, 4),       # 128 units: 512
+        (12, 32, 8, 128, 2048, F32, 8),       # 96 units do not divide 512: 768
+        (2, 64, 8, 128, 8192, F32, 43),       # 8 heads per row set: 768 aimed at, 192-position splits
+        (1, 8, 2, 64, 8192, F32, 256),        # 2 units of 4 heads: 768 workgroups aimed at, 32-position splits
+    ]
+    monkeypatch.setenv("GQA_KERNEL", "valu")
+    for B, H, G, d, L, dt, S, *grid in valu_cases:
+        assert lib.gqa_decode_workspace_size(B, H, G, d, L, dt) == _decode_ws(B, H, S, d, *grid), (B, H, G, d, L, dt, S)
+    assert lib.gqa_decode_workspace_size(1, 8, 2, 64, 256, F32) == 0     # 8 -> 1 split by the estimate
+    monkeypatch.delenv("GQA_KERNEL")
     monkeypatch.setenv("GQA_ORDER", "0")  # no dispatch order: no order region
     assert lib.gqa_decode_workspace_size(64, 64, 8, 128, 32768, BF16) == _decode_ws(64, 64, 4, 128)
     # one split: no workspace
-    assert lib.gqa_decode_workspace_size(1, 8, 2, 64, 256, F32) == 0     # VALU: 8 -> 1 split by the estimate
     assert lib.gqa_decode_workspace_size(4, 32, 32, 64, 512, BF16) == 0  # VALU r = 1: 2 -> 1
-    monkeypatch.setenv("GQA_TARGET_WGS", "256")  # a plain target: 32-position floor, 8 splits
+    monkeypatch.setenv("GQA_TARGET_WGS", "256")  # a plain target: the floors, 64 and 32 positions
+    assert lib.gqa_decode_workspace_size(1, 8, 2, 64, 256, F32) == _decode_ws(1, 8, 4, 64)
+    monkeypatch.setenv("GQA_KERNEL", "valu")
     assert lib.gqa_decode_workspace_size(1, 8, 2, 64, 256, F32) == _decode_ws(1, 8, 8, 64)
+    monkeypatch.delenv("GQA_KERNEL")
     monkeypatch.delenv("GQA_TARGET_WGS")
     assert lib.gqa_decode_workspace_size(32, 64, 8, 64, 2048, BF16) == 0
     assert lib.gqa_decode_workspace_size(128, 32, 1, 128, 1024, BF16) == 0  # 2 head chunks, one split each
@@ -244,7 +265,12 @@ def test_plan_lookup_cost(lib):
 def test_kernel_selection(lib, monkeypatch):
     monkeypatch.delenv("GQA_KERNEL", raising=False)
     assert lib.gqa_decode_kernel_kind(16, 32, 8, 128, 4096, BF16) == 1
-    assert lib.gqa_decode_kernel_kind(1, 8, 2, 64, 256, F32) == 0
+    assert lib.gqa_decode_kernel_kind(1, 8, 2, 64, 256, F32) == 1     # binary32, r = 4: matrix cores
+    assert lib.gqa_decode_kernel_kind(8, 48, 4, 128, 4096, F32) == 1  # r = 12
+    assert lib.gqa_decode_kernel_kind(8, 32, 16, 128, 8192, F32) == 0  # r = 2: the VALU kernel
+    assert lib.gqa_decode_kernel_kind(8, 32, 32, 128, 4096, F32) == 0  # r = 1
+    assert lib.gqa_decode_kernel_kind(1, 32, 1, 64, 256, F32) == 1     # r = 32: two head blocks
+    assert lib.gqa_decode_kernel_kind(1, 128, 1, 64, 256, F32) == 0    # r = 128
     assert lib.gqa_decode_kernel_kind(1, 128, 1, 64, 256, BF16) == 0  # more than 64 heads per group
     assert lib.gqa_decode_kernel_kind(32, 64, 64, 64, 2048, BF16) == 1  # r = 1, 1 GiB of K and V: matrix cores
     assert lib.gqa_decode_kernel_kind(2, 8, 8, 128, 4096, BF16) == 1    # r = 1, 32 MiB
@@ -255,7 +281,8 @@ def test_kernel_selection(lib, monkeypatch):
     assert lib.gqa_decode_kernel_kind(16, 32, 8, 128, 4096, BF16) == 0
     monkeypatch.setenv("GQA_KERNEL", "mfma")
     assert lib.gqa_decode_kernel_kind(4, 32, 32, 64, 512, BF16) == 1
-    assert lib.gqa_decode_kernel_kind(1, 8, 2, 64, 256, F32) == 0  # no fp32 matrix-core path
+    assert lib.gqa_decode_kernel_kind(8, 32, 16, 128, 8192, F32) == 1  # forced: binary32 at r = 2
+    assert lib.gqa_decode_kernel_kind(1, 64, 1, 64, 256, F32) == 1     # r = 64: four head chunks
 
 
 def test_meanpool_argument_errors(lib):

@@ -132,6 +132,55 @@ def test_small_parity(env, case, dtype, kernel, chunk, merge):
     check(out, oracle_out(q, k, v, lens_t, scale), dtype, "%s %s chunk=%s %s" % (dtype, kernel, chunk, case))
 
 
+# Binary32 on the matrix cores (v_mfma_f32_16x16x4_f32; the default for 3..64
+# heads per K/V head), forced with GQA_KERNEL=mfma on every small shape: r = 1
+# and 2 pad the head block with zero queries, r = 24 and 64 take a workgroup
+# per block of 16 heads.  Every split and merge path, then the window, the
+# cache append, ragged lengths at tile edges and a dispatch order.
+F32_MFMA = SMALL
+
+
+@pytest.mark.parametrize("case", F32_MFMA, ids=lambda c: "B%d_H%d_G%d_d%d_L%d" % c[:5])
+@pytest.mark.parametrize("chunk", [None, 32, 128, 100000])
+@pytest.mark.parametrize("merge", ["fused", "kernel", "wide"])
+def test_f32_matrix_cores(env, case, chunk, merge):
+    B, H, G, d, L, lens = case
+    env(GQA_KERNEL="mfma", GQA_CHUNK=chunk, GQA_MERGE="kernel" if merge == "kernel" else None,
+        GQA_FUSED_MAX_SPLITS=1 if merge == "wide" else None)
+    assert gqa.decode_kernel_kind(B, H, G, d, L, gqa.GQA_F32) == 1
+    q, k, v, lens_t, scale = rand_case(B, H, G, d, L, lens, "f32", seed=sum(case[:5]) + 3 * len(lens))
+    out = run_gpu(q, k, v, lens_t, scale)
+    check(out, oracle_out(q, k, v, lens_t, scale), "f32", "f32 mfma chunk=%s %s %s" % (chunk, merge, case))
+
+
+@pytest.mark.parametrize("chunk", [None, 64])
+def test_f32_matrix_cores_window_append_order(env, chunk):
+    B, H, G, d, L = 5, 32, 8, 128, 700
+    lens = [700, 1, 17, 256, 513]
+    env(GQA_KERNEL="mfma", GQA_CHUNK=chunk)
+    q, k, v, lens_t, scale = rand_case(B, H, G, d, L, lens, "f32", seed=41)
+    for W in (1, 15, 16, 17, 300):
+        out = gqa.decode_window(q, k, v, lens_t, scale, window=W)
+        torch.cuda.synchronize()
+        ref = oracle.decode(q.cpu(), k.cpu(), v.cpu(), lens_t.cpu(), scale, window=W)
+        check(out, ref, "f32", "f32 mfma window %d chunk=%s" % (W, chunk))
+    # the append writes position len-1 of each sequence (lengths count the new token)
+    k_new = torch.randn(B, G, d, device=DEV)
+    v_new = torch.randn(B, G, d, device=DEV)
+    k2, v2 = k.clone(), v.clone()
+    out = gqa.decode_append(q, k_new, v_new, k2, v2, lens_t, scale)
+    torch.cuda.synchronize()
+    ref, rk, rv = oracle.decode_append(q.cpu(), k_new.cpu(), v_new.cpu(), k.cpu(), v.cpu(), lens_t.cpu(), scale)
+    check(out, ref, "f32", "f32 mfma append chunk=%s" % chunk)
+    for b, n in enumerate(lens):
+        assert np.array_equal(k2[b, :, :n].cpu().numpy(), np.asarray(rk)[b, :, :n])
+        assert np.array_equal(v2[b, :, :n].cpu().numpy(), np.asarray(rv)[b, :, :n])
+    # several rounds of workgroups, taken largest first by the order kernel
+    env(GQA_KERNEL="mfma", GQA_CHUNK=32, GQA_ORDER=1)
+    out = run_gpu(q, k, v, lens_t, scale)
+    check(out, oracle_out(q, k, v, lens_t, scale), "f32", "f32 mfma ordered")
+
+
 # Many splits per sequence: beyond 32 the splits are merged by the wide merge
 # kernel (a workgroup per sequence, head and 32 dimensions; 32 slices of
 # splits folded in order).  Sequences with few and with many splits side by
@@ -273,10 +322,12 @@ PLAN_SHAPES = [
     (48, 32, 8, 128, 2048, "bf16"),    # 384 units: 2 splits, three full rounds
     (4, 32, 1, 128, 16384, "bf16"),    # 32 heads per K/V head: 1 head chunk, 64 splits (wide merge)
     (64, 64, 1, 64, 4096, "bf16"),     # 64 heads per K/V head: 2 head chunks
-    (12, 32, 8, 128, 2048, "f32"),     # binary32, VALU kernel aiming at 768 workgroups
-    (4, 32, 8, 128, 8192, "f32"),      # binary32, 32 units divide 512: 512 workgroups
-    (64, 32, 8, 128, 2048, "f32"),     # binary32, 512 units: one split each
-    (1, 8, 2, 64, 1024, "f32"),        # VALU one-round grid: 32 -> 8 splits by the estimate
+    (12, 32, 8, 128, 2048, "f32"),     # binary32 matrix cores, 96 units: 5 splits, two full rounds
+    (4, 32, 8, 128, 8192, "f32"),      # binary32 matrix cores, 32 units: 8 splits
+    (64, 32, 8, 128, 2048, "f32"),     # binary32 matrix cores, 512 units: one split each
+    (1, 8, 2, 64, 1024, "f32"),        # binary32 matrix cores, one-round grid: 16 splits of 64 by the estimate
+    (2, 64, 1, 64, 4096, "f32"),       # binary32 matrix cores, r = 64: four head chunks
+    (8, 32, 16, 128, 4096, "f32"),     # binary32 r = 2: the VALU kernel
     (4, 32, 32, 64, 512, "bf16"),      # VALU (r = 1): 2 -> 1 split by the estimate
     (64, 64, 8, 128, 16384, "bf16"),   # 8192-position split cap: 2 splits, 1024 workgroups
 ]
@@ -285,7 +336,7 @@ PLAN_SHAPES = [
 @pytest.mark.parametrize("shape", PLAN_SHAPES, ids=lambda c: "B%d_H%d_G%d_d%d_L%d_%s" % c)
 def test_default_plan_shapes(env, shape):
     """Shapes whose default plans come from the split-count, head-chunk,
-    binary32 target and VALU split estimates and the split cap, against the
+    binary32 and VALU split estimates and the split cap, against the
     oracle on sampled sequences (ragged lengths keep every split path busy)."""
     B, H, G, d, L, dtype = shape
     gen = torch.Generator().manual_seed(B * 131 + L)
