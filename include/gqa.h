@@ -298,9 +298,10 @@ const char *gqa_last_hip_error(void);
 
 /*
  * Which decode kernel a shape runs on: 0 = VALU kernel (binary32 or bfloat16
- * dot products on the vector ALUs), 1 = MFMA kernel (bfloat16 matrix cores).
- * Returns -1 for arguments gqa_decode would reject.  (The tuning override
- * GQA_KERNEL=valu|mfma of gqa_measure.h forces a kernel; bfloat16 only for mfma.)
+ * dot products on the vector ALUs), 1 = a matrix-core kernel (bfloat16, or
+ * binary32 with 3..64 query heads per K/V head).  Returns -1 for arguments
+ * gqa_decode would reject.  (The tuning override GQA_KERNEL=valu|mfma of
+ * gqa_measure.h forces a kernel; mfma up to 64 query heads per K/V head.)
  */
 int gqa_decode_kernel_kind(int B, int H, int G, int d, int Lmax, gqa_dtype dtype);
 

@@ -36,7 +36,7 @@ gqa_status gqa_stream_read(const void *buf, size_t bytes, int nontemporal, int g
  * Launch-plan overrides.  The library reads its GQA_* environment variables
  * (GQA_KERNEL=valu|mfma, GQA_CHUNK, GQA_TARGET_WGS, GQA_MAX_CHUNK,
  * GQA_FUSED_MAX_SPLITS, GQA_WAVES, GQA_HEAD_SPLIT, GQA_CONTIG, GQA_TEMPORAL,
- * GQA_MERGE=kernel, GQA_ORDER, GQA_VALU_PIECES, GQA_LINEAR_*) once, when it
+ * GQA_MERGE=kernel, GQA_ORDER, GQA_ARRIVE, GQA_VALU_PIECES, GQA_LINEAR_*) once, when it
  * is loaded; unset, every call takes the measured default plan.  Calls never
  * read the environment themselves.  gqa_tuning_reload() reads the variables
  * again and drops the plans cached per shape.  It must not run while another

@@ -43,11 +43,13 @@ SEQUENCES = [
     [(16, 32, 8, 128, 4096, [4096, 1, 2049] + [4096 - 250 * i for i in range(13)], "bf16", 1),  # matrix cores, 2 splits
      (3, 8, 2, 64, 700, [700, 1, 333], "bf16", 2)],                                             # 3 splits
     [(2, 8, 1, 128, 40000, [40000, 9000], "bf16", 3),   # 157 splits: the wide merge kernel
-     (1, 8, 2, 64, 1024, [1000], "f32", 4)],            # VALU kernel, binary32, 8 splits
+     (1, 8, 2, 64, 1024, [1000], "f32", 4)],            # binary32 matrix cores, 16 splits
+    [(4, 32, 16, 128, 3000, [3000, 17, 2999, 1500], "f32", 5),   # binary32 r = 2: the VALU kernel, split
+     (2, 16, 4, 128, 900, [900, 450], "f32", 6)],                 # binary32 matrix cores, split
 ]
 
 
-@pytest.mark.parametrize("seq", SEQUENCES, ids=["fused_merge", "wide_merge_then_f32"])
+@pytest.mark.parametrize("seq", SEQUENCES, ids=["fused_merge", "wide_merge_then_f32", "f32_valu_then_mfma"])
 def test_noalloc_matches_workspace_decode(seq):
     lib = gqa.load_library()
     for (B, H, G, d, L, lens, dtype, seed) in seq:
