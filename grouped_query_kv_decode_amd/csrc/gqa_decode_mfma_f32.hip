@@ -34,20 +34,6 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// max / sum over the four lanes l, l^16, l^32, l^48 (one head's lane groups)
-__device__ __forceinline__ float group_max4(float x) {
-  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float group_sum4(float x) {
-  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
 template <int D, bool NT>
 __global__ __launch_bounds__(256) void decode_mfma_f32(DecodeParams p) {
   static_assert(D == 64 || D == 128, "head dim");
@@ -185,7 +171,7 @@ __global__ __launch_bounds__(256) void decode_mfma_f32(DecodeParams p) {
       if (tail && tt + 4 * c + i >= t1) sc[i] = kNegInf;
     }
     float mt = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-    mt = group_max4(mt);
+    mt = group_max(mt);
     if (__builtin_amdgcn_ballot_w64(mt > m_run + kSlack)) {
       const float mn = mt > m_run + kSlack ? mt : m_run;
       const float alpha = fast_exp2(m_run - safe_shift(mn));
@@ -251,7 +237,7 @@ __global__ __launch_bounds__(256) void decode_mfma_f32(DecodeParams p) {
     }
   }
 
-  l_run = group_sum4(l_run);
+  l_run = group_sum(l_run);
 
   // Merge the waves through LDS in wave order (deterministic).
   constexpr int LD = D + 4;

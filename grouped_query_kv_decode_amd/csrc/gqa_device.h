@@ -55,6 +55,21 @@ __device__ __forceinline__ uint4 stream_load(const uint4 *p) {
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+// Max / sum over the four lanes l, l^16, l^32, l^48 (the lane groups of one
+// matrix-core output column: one head in the decode kernels).
+__device__ __forceinline__ float group_max(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float group_sum(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Shift used with a running maximum: keeps exp2(x - shift) free of
 // (-inf) - (-inf) when nothing has been seen yet.
 __device__ __forceinline__ float safe_shift(float m) { return m == kNegInf ? 0.f : m; }
