@@ -872,14 +872,15 @@ def test_random_configurations(env, case):
         check(out, oracle_out(q, k, v, lt, scale), dtype, what)
 
 
-def _random_plans(n, seed):
+def _random_plans(n, seed, binary32=False, first=0):
     """Random shapes as above, each with random plan settings: split length
     (down to one tile, so up to ~250 splits), dispatch order forced on, the
     wide merge forced, plain or non-temporal cache loads, head split; larger
-    batches, so that some grids exceed 1024 workgroups."""
+    batches, so that some grids exceed 1024 workgroups.  binary32: every case
+    in binary32, with the kernel drawn too (the plan's, or either forced)."""
     rng = np.random.default_rng(seed)
     cases = []
-    for i in range(n):
+    for i in range(first, first + n):
         d = int(rng.choice([64, 128]))
         G = int(rng.choice([1, 2, 4, 8]))
         r = int(rng.choice([1, 2, 3, 4, 8, 16, 24, 64]))
@@ -887,7 +888,7 @@ def _random_plans(n, seed):
         Lmax = int(rng.integers(1, 8000))
         lens = [int(x) for x in rng.integers(0, Lmax + 1, size=B)]
         lens[0] = Lmax
-        dtype = "bf16" if rng.random() < 0.8 else "f32"
+        dtype = "f32" if binary32 or rng.random() >= 0.8 else "bf16"
         window = int(rng.integers(1, Lmax + 40)) if rng.random() < 0.25 else 0
         append = bool(rng.random() < 0.25)
         plan = {
@@ -898,11 +899,14 @@ def _random_plans(n, seed):
             "GQA_HEAD_SPLIT": int(rng.choice([1, 2, 4])) if rng.random() < 0.2 else None,
             "GQA_MERGE": "kernel" if rng.random() < 0.15 else None,
         }
+        if binary32:
+            plan["GQA_KERNEL"] = [None, "mfma", "valu"][int(rng.integers(0, 3))]
         cases.append((i, B, G * r, G, d, Lmax, lens, dtype, window, append, plan))
     return cases
 
 
-@pytest.mark.parametrize("case", _random_plans(48, 4242), ids=lambda c: "plan%02d" % c[0])
+@pytest.mark.parametrize("case", _random_plans(48, 4242) + _random_plans(24, 5151, binary32=True, first=100),
+                         ids=lambda c: "plan%02d" % c[0] if c[0] < 100 else "f32plan%02d" % (c[0] - 100))
 def test_random_plans(env, case):
     i, B, H, G, d, Lmax, lens, dtype, window, append, plan = case
     env(**plan)
