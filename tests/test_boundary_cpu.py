@@ -34,6 +34,46 @@ def test_headers_present():
     assert [os.path.basename(h) for h in HEADERS] == ["gqa.h", "gqa_measure.h"]
 
 
+C_CLIENT = r"""
+#include <stdio.h>
+#include "gqa.h"
+#include "gqa_measure.h"
+int main(void) {
+  size_t ws = gqa_decode_workspace_size(16, 32, 8, 128, 4096, GQA_BF16);
+  gqa_status empty = gqa_decode(NULL, NULL, NULL, NULL, 0, 32, 8, 128, 4096, 0.088f, GQA_BF16, NULL, NULL, 0, NULL);
+  gqa_status bad = gqa_decode(NULL, NULL, NULL, NULL, 1, 32, 6, 128, 4096, 0.088f, GQA_BF16, NULL, NULL, 0, NULL);
+  printf("%zu %d %d %d %d\n", ws, (int)empty, (int)bad, gqa_decode_kernel_kind(16, 32, 8, 128, 4096, GQA_F32),
+         (int)(GQA_NOALLOC_SCRATCH_BYTES >> 20));
+  return 0;
+}
+"""
+
+
+@pytest.mark.parametrize("compiler,std", [("gcc", "-std=c11"), ("g++", "-std=c++17")])
+def test_headers_serve_a_plain_c_client(tmp_path, compiler, std):
+    """Both headers compile as strict C11 (and as C++17) with every warning
+    an error, and a client links libgqa.so and calls it through them (host
+    paths only: sizing, an empty batch, a rejected shape, the kernel choice)."""
+    import shutil
+    import subprocess
+    if shutil.which(compiler) is None:
+        pytest.skip(compiler + " not installed")
+    src = tmp_path / ("client.c" if compiler == "gcc" else "client.cpp")
+    src.write_text(C_CLIENT)
+    exe = tmp_path / "client"
+    pkg = os.path.dirname(gqa.library_path())
+    cmd = [compiler, std, "-Wall", "-Wextra", "-Werror", "-pedantic", "-D__HIP_PLATFORM_AMD__",
+           "-isystem", "/opt/rocm/include", "-I" + os.path.join(ROOT, "include"), str(src),
+           "-L" + pkg, "-lgqa", "-Wl,-rpath," + pkg, "-o", str(exe)]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert out.returncode == 0, out.stderr
+    ws, empty, bad, kind, scratch_mib = (int(x) for x in out.stdout.split())
+    assert ws == _decode_ws(16, 32, 2, 128)  # the Mistral-7B shape's plan: 2 splits
+    assert (empty, bad, kind, scratch_mib) == (OK, SHAPE, 1, 32)
+
+
 def test_header_declares_the_binding_list():
     assert declared_functions() == sorted(gqa.EXPORTED)
 
