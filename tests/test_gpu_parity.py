@@ -519,6 +519,34 @@ def test_non_default_stream(env):
     check(out, oracle_out(q, k, v, lens, scale), "bf16", "side stream")
 
 
+def test_concurrent_streams(env):
+    """Two side streams (default priority) each running split plans at the
+    same time, with no synchronisation between them: the binding keeps one
+    workspace per stream, so the arrival counters and partials of the two
+    never mix.  Every call bit-equal to the same call run alone."""
+    env(GQA_CHUNK=128)
+    a = rand_case(3, 32, 8, 128, 900, [900, 400, 129], "bf16", seed=14)
+    b = rand_case(4, 16, 4, 128, 1000, [1000, 999, 513, 1], "f32", seed=15)
+    ref_a = run_gpu(*a).clone()
+    ref_b = run_gpu(*b).clone()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for _ in range(5):
+        with torch.cuda.stream(s1):
+            oa = gqa.decode(*a)
+        with torch.cuda.stream(s2):
+            ob = gqa.decode(*b)
+        outs.append((oa, ob))
+    s1.synchronize()
+    s2.synchronize()
+    for oa, ob in outs:
+        assert torch.equal(oa, ref_a) and torch.equal(ob, ref_b)
+    check(ref_a, oracle_out(*a), "bf16", "stream a")
+    check(ref_b, oracle_out(*b), "f32", "stream b")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_equal_queries_in_a_group(env, dtype):
     q, k, v, lens, scale = rand_case(1, 16, 4, 128, 500, [500], dtype, seed=13)
