@@ -29,10 +29,10 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p, int heads_pe
 
 // Many splits (up to 256 per sequence, for few and long sequences): one
 // workgroup per (sequence, head, 32 output dimensions), 256 threads = 8 groups
-// of 4 dimensions x 32 slices of consecutive splits.  Each thread folds its
-// slice; the slices are then folded in slice order through LDS, so the result
-// is deterministic, and no thread reads more than ceil(nsplit / 32) partials
-// (one batch of loads at 256 splits).
+// of 4 dimensions x 32 slices of consecutive splits.  Each thread combines its
+// slice; the slices are then combined in slice order through LDS, so the
+// result is deterministic, and no thread reads more than ceil(nsplit / 32)
+// partials (one batch of loads at 256 splits).
 struct Fold {
   float M = kNegInf, L = 0.f, o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
   __device__ __forceinline__ void add(float m, float l, float x0, float x1, float x2, float x3) {
@@ -64,12 +64,15 @@ __global__ __launch_bounds__(256) void merge_wide_kernel(DecodeParams p) {
   const float *ml = reinterpret_cast<const float *>(p.ws_ml + (size_t)bh * p.S);
   const float *o = p.ws_o + (size_t)bh * p.S * D + c;
   Fold f;
-  for (int i0 = 0; i0 < cnt; i0 += kBatch) {
+  if (cnt <= kBatch) {
+    // One batch (every plan of at most 512 splits): the slice's maximum
+    // first, then its weighted sums, whose exp2 terms are independent (the
+    // running fold below chains two exp2 per split).
     float2 h[kBatch], x[kBatch], y[kBatch];
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
-      if (i0 + i < cnt) {
-        const int s = first + i0 + i;
+      if (i < cnt) {
+        const int s = first + i;
         h[i] = load_pair(ml + 2 * s);
         x[i] = load_pair(o + (size_t)s * D);
         y[i] = load_pair(o + (size_t)s * D + 2);
@@ -77,7 +80,35 @@ __global__ __launch_bounds__(256) void merge_wide_kernel(DecodeParams p) {
     }
 #pragma unroll
     for (int i = 0; i < kBatch; ++i)
-      if (i0 + i < cnt) f.add(h[i].x, h[i].y, x[i].x, x[i].y, y[i].x, y[i].y);
+      if (i < cnt) f.M = fmaxf(f.M, h[i].x);
+    const float sh = safe_shift(f.M);
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      if (i < cnt) {
+        const float a = fast_exp2(h[i].x - sh);
+        f.L += h[i].y * a;
+        f.o0 += x[i].x * a;
+        f.o1 += x[i].y * a;
+        f.o2 += y[i].x * a;
+        f.o3 += y[i].y * a;
+      }
+    }
+  } else {
+    for (int i0 = 0; i0 < cnt; i0 += kBatch) {
+      float2 h[kBatch], x[kBatch], y[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        if (i0 + i < cnt) {
+          const int s = first + i0 + i;
+          h[i] = load_pair(ml + 2 * s);
+          x[i] = load_pair(o + (size_t)s * D);
+          y[i] = load_pair(o + (size_t)s * D + 2);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i)
+        if (i0 + i < cnt) f.add(h[i].x, h[i].y, x[i].x, x[i].y, y[i].x, y[i].y);
+    }
   }
   __shared__ float sm[kSlices][8][6];
   float *e = sm[k][q];
@@ -89,13 +120,23 @@ __global__ __launch_bounds__(256) void merge_wide_kernel(DecodeParams p) {
   e[5] = f.o3;
   __syncthreads();
   if (k != 0) return;
-  Fold t;
-  for (int kk = 0; kk < kSlices && kk * per < nsplit; ++kk) {
+  // The slices in slice order, again maximum first, then the weighted sums.
+  const int used = min(kSlices, (nsplit + per - 1) / per);
+  float M = kNegInf;
+  for (int kk = 0; kk < used; ++kk) M = fmaxf(M, sm[kk][q][0]);
+  const float sh = safe_shift(M);
+  float L = 0.f, o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+  for (int kk = 0; kk < used; ++kk) {
     const float *v = sm[kk][q];
-    t.add(v[0], v[1], v[2], v[3], v[4], v[5]);
+    const float a = fast_exp2(v[0] - sh);
+    L += v[1] * a;
+    o0 += v[2] * a;
+    o1 += v[3] * a;
+    o2 += v[4] * a;
+    o3 += v[5] * a;
   }
-  const float inv = 1.f / t.L;
-  Store<T>::four(p.out, (size_t)bh * D + c, t.o0 * inv, t.o1 * inv, t.o2 * inv, t.o3 * inv);
+  const float inv = 1.f / L;
+  Store<T>::four(p.out, (size_t)bh * D + c, o0 * inv, o1 * inv, o2 * inv, o3 * inv);
 }
 
 template <typename T>
