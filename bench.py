@@ -618,7 +618,8 @@ def summarize_rocprof(d):
 
 # the per-phase timeline: the bench default, the small calls, and the largest T5-XXL
 # point that needs no split (workload, window)
-TIMELINE_CASES = [("mistral7b_bf16_B16_H32_G8_d128_L4096", 0), ("t5xxl_bf16_B32_H64_G1_d64_L2048", 0),
+TIMELINE_CASES = [("tiny_f32_B1_H8_G2_d64_L256", 0),
+                  ("mistral7b_bf16_B16_H32_G8_d128_L4096", 0), ("t5xxl_bf16_B32_H64_G1_d64_L2048", 0),
                   ("t5xxl_bf16_B32_H64_G4_d64_L2048", 0), ("t5xxl_bf16_B32_H64_G8_d64_L2048", 0),
                   ("mistral7b_bf16_B16_H32_G8_d128_L4096", 1024)]
 

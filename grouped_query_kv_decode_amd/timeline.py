@@ -3,9 +3,9 @@
     python -m grouped_query_kv_decode_amd.timeline build     # on any machine (hipcc cross-compiles)
     python bench.py --timeline                               # on the GPU
 
-build() copies the library sources, inserts wall-clock stamps into the
-matrix-core decode kernel and links the copy as libgqa_timeline.so next to
-libgqa.so.  The stamps are s_memrealtime reads (a constant 100 MHz counter
+build() copies the library sources, inserts wall-clock stamps into the two
+matrix-core decode kernels (bfloat16 and binary32) and links the copy as
+libgqa_timeline.so next to libgqa.so.  The stamps are s_memrealtime reads (a constant 100 MHz counter
 shared by the whole GPU) stored by lane 0 of each wave of the first 8192
 workgroups: kernel entry, first tile multiplied, tile loop done, output or
 partial stores issued, arrival ticket taken, end (after the merge for the
@@ -31,38 +31,52 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB = os.path.join(PKG, "libgqa_timeline.so")
 _SLOTS = 8192 * 4 * 8
 
-# (anchor in gqa_decode_mfma.hip, replacement): each anchor must occur once
-_STAMPS = [
-    ("namespace gqa {\nnamespace {\n",
-     "__device__ unsigned long long tl_buf[8192 * 4 * 8];\n"
-     "namespace gqa {\nnamespace {\n"
-     "__device__ __forceinline__ void tl_put(int e, unsigned long long v) {\n"
-     "  if ((threadIdx.x & 63) == 0 && blockIdx.x < 8192 && (threadIdx.x >> 6) < 4)\n"
-     "    tl_buf[(blockIdx.x * 4 + (threadIdx.x >> 6)) * 8 + e] = v;\n"
-     "}\n"
-     "__device__ __forceinline__ void tl_stamp(int e) { tl_put(e, __builtin_amdgcn_s_memrealtime()); }\n"),
-    ("  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;\n  const int c = lane >> 4, nn = lane & 15;\n",
-     "  tl_stamp(0);\n  tl_put(4, 0);\n  tl_put(6, 0);\n"
-     "  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;\n  const int c = lane >> 4, nn = lane & 15;\n"
-     "  bool tl_first = false;\n"),
-    ("    pv_steps<0, DB, HB>(o, T.vR, pB);\n  };",
-     "    pv_steps<0, DB, HB>(o, T.vR, pB);\n    if (!tl_first) {\n      tl_first = true;\n      tl_stamp(1);\n    }\n  };"),
-    ("  for (int hb = 0; hb < HB; ++hb) l[hb] = group_sum(l[hb]);\n",
-     "  for (int hb = 0; hb < HB; ++hb) l[hb] = group_sum(l[hb]);\n  tl_stamp(2);\n"),
-    ("  if (nsplit == 1 || !p.fused) return;\n"
-     "  if (!arrive_last(p.ws_cnt + ((size_t)b * p.G + g) * p.HC + hc, nsplit, p.arrive_acqrel)) return;\n"
-     "  merge_heads<__bf16, D>(p, b, head0, rw, nsplit);",
-     "  tl_stamp(3);\n"
-     "  if (nsplit == 1 || !p.fused) {\n    tl_stamp(5);\n    return;\n  }\n"
-     "  const bool tl_last = arrive_last(p.ws_cnt + ((size_t)b * p.G + g) * p.HC + hc, nsplit, p.arrive_acqrel);\n"
-     "  tl_stamp(4);\n"
-     "  if (!tl_last) {\n    tl_stamp(5);\n    return;\n  }\n"
-     "  merge_heads<__bf16, D>(p, b, head0, rw, nsplit);\n"
-     "  __builtin_amdgcn_s_waitcnt(0);\n  tl_stamp(5);\n  tl_put(6, 1);"),
+# (anchor, replacement) per kernel source: each anchor must occur once.  The
+# two kernels are separate code objects, so each gets its own stamp buffer
+# and reader.
+
+
+def _stamps(buf, tp, merge_call, pv_end):
+    return [
+        ("namespace gqa {\nnamespace {\n",
+         "__device__ unsigned long long %s[8192 * 4 * 8];\n" % buf +
+         "namespace gqa {\nnamespace {\n"
+         "__device__ __forceinline__ void tl_put(int e, unsigned long long v) {\n"
+         "  if ((threadIdx.x & 63) == 0 && blockIdx.x < 8192 && (threadIdx.x >> 6) < 4)\n"
+         "    %s[(blockIdx.x * 4 + (threadIdx.x >> 6)) * 8 + e] = v;\n" % buf +
+         "}\n"
+         "__device__ __forceinline__ void tl_stamp(int e) { tl_put(e, __builtin_amdgcn_s_memrealtime()); }\n"),
+        ("  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;\n  const int c = lane >> 4, nn = lane & 15;\n",
+         "  tl_stamp(0);\n  tl_put(4, 0);\n  tl_put(6, 0);\n"
+         "  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;\n  const int c = lane >> 4, nn = lane & 15;\n"
+         "  bool tl_first = false;\n"),
+        (pv_end + "\n  };",
+         pv_end + "\n    if (!tl_first) {\n      tl_first = true;\n      tl_stamp(1);\n    }\n  };"),
+        (tp, tp + "  tl_stamp(2);\n"),
+        ("  if (nsplit == 1 || !p.fused) return;\n"
+         "  if (!arrive_last(p.ws_cnt + ((size_t)b * p.G + g) * p.HC + hc, nsplit, p.arrive_acqrel)) return;\n"
+         "  " + merge_call,
+         "  tl_stamp(3);\n"
+         "  if (nsplit == 1 || !p.fused) {\n    tl_stamp(5);\n    return;\n  }\n"
+         "  const bool tl_last = arrive_last(p.ws_cnt + ((size_t)b * p.G + g) * p.HC + hc, nsplit, p.arrive_acqrel);\n"
+         "  tl_stamp(4);\n"
+         "  if (!tl_last) {\n    tl_stamp(5);\n    return;\n  }\n"
+         "  " + merge_call + "\n"
+         "  __builtin_amdgcn_s_waitcnt(0);\n  tl_stamp(5);\n  tl_put(6, 1);"),
+    ]
+
+
+_KERNELS = [  # (source, stamp buffer, reader)
+    ("gqa_decode_mfma.hip", "tl_buf", "gqa_timeline_read",
+     _stamps("tl_buf", "  for (int hb = 0; hb < HB; ++hb) l[hb] = group_sum(l[hb]);\n",
+             "merge_heads<__bf16, D>(p, b, head0, rw, nsplit);", "    pv_steps<0, DB, HB>(o, T.vR, pB);")),
+    ("gqa_decode_mfma_f32.hip", "tl_buf_f32", "gqa_timeline_read_f32",
+     _stamps("tl_buf_f32", "  l_run = group_sum(l_run);\n", "merge_heads<float, D>(p, b, head0, rw, nsplit);",
+             "        for (int e = 0; e < 4; ++e) o[4 * m + e] = mfma4(T.vR[i][m][e], pw[i], o[4 * m + e]);")),
 ]
 _READER = """
-extern "C" int gqa_timeline_read(void *host, size_t bytes) {
-  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(tl_buf), bytes, 0, hipMemcpyDeviceToHost);
+extern "C" int %s(void *host, size_t bytes) {
+  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(%s), bytes, 0, hipMemcpyDeviceToHost);
 }
 """
 
@@ -74,14 +88,15 @@ def build(verbose: bool = True) -> str:
     csrc = os.path.join(work, "csrc")
     shutil.rmtree(work, ignore_errors=True)
     shutil.copytree(b.CSRC, csrc)
-    path = os.path.join(csrc, "gqa_decode_mfma.hip")
-    src = open(path).read()
-    for anchor, repl in _STAMPS:
-        if src.count(anchor) != 1:
-            raise RuntimeError("timeline: anchor not found once in gqa_decode_mfma.hip: %r" % anchor[:60])
-        src = src.replace(anchor, repl)
-    with open(path, "w") as f:
-        f.write(src + _READER)
+    for name, buf, reader, stamps in _KERNELS:
+        path = os.path.join(csrc, name)
+        src = open(path).read()
+        for anchor, repl in stamps:
+            if src.count(anchor) != 1:
+                raise RuntimeError("timeline: anchor not found once in %s: %r" % (name, anchor[:60]))
+            src = src.replace(anchor, repl)
+        with open(path, "w") as f:
+            f.write(src + _READER % (reader, buf))
     def compile_one(item):
         name, extra = item
         obj = os.path.join(work, os.path.splitext(name)[0] + ".o")
@@ -135,7 +150,8 @@ def run(cases, tick_us: float = 0.01, groups: int = 30):
     if not os.path.exists(LIB):
         raise RuntimeError("%s not built: python -m grouped_query_kv_decode_amd.timeline build" % LIB)
     lib = gqa.load_library(LIB)
-    lib.gqa_timeline_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    for _, _, reader, _ in _KERNELS:
+        getattr(lib, reader).argtypes = [ctypes.c_void_p, ctypes.c_size_t]
     saved = gqa._lib
     gqa._lib = lib
     host = np.zeros(_SLOTS, dtype=np.uint64)
@@ -144,6 +160,10 @@ def run(cases, tick_us: float = 0.01, groups: int = 30):
     try:
         for name, window in cases:
             w = wl.WORKLOADS[name]
+            code = gqa.GQA_F32 if w.dtype == "f32" else gqa.GQA_BF16
+            if gqa.decode_kernel_kind(w.B, w.H, w.G, w.d, w.Lmax, code) != 1:
+                raise RuntimeError("timeline: %s does not run on a matrix-core kernel" % name)
+            read = lib.gqa_timeline_read_f32 if w.dtype == "f32" else lib.gqa_timeline_read
             kvb = 2 * w.B * w.G * w.Lmax * w.d * (4 if w.dtype == "f32" else 2)
             rot = min(64, max(1, math.ceil((1 << 30) / kvb)))
             decs = [gqa.Decoder(*wl.make_inputs(w, dev, pad="none", seed_offset=i), w.scale, window=window)
@@ -159,7 +179,7 @@ def run(cases, tick_us: float = 0.01, groups: int = 30):
                     decs[(it * 10 + j) % rot]()
                 e1.record()
                 torch.cuda.synchronize()
-                if lib.gqa_timeline_read(host.ctypes.data, host.nbytes) != 0:
+                if read(host.ctypes.data, host.nbytes) != 0:
                     raise RuntimeError("timeline read failed")
                 ph = _phases(host.reshape(8192, 4, 8).astype(np.int64), tick_us)
                 ph["call_us"] = e0.elapsed_time(e1) * 1e3 / 10
