@@ -137,10 +137,13 @@ gqa_status check_shape(int B, int H, int G, int d, int Lmax, gqa_dtype dt) {
 // Decode launch plan (tuned on MI355X with the workload sweep):
 //  - kernel: bfloat16 uses the matrix-core kernel for r = H/G in 2..64, and
 //    for r = 1 on calls that stream at least 32 MiB of K and V (smaller MHA
-//    calls take the VALU kernel, whose one-round plan splits less); fp32
-//    always uses the VALU kernel.  GQA_KERNEL=valu|mfma overrides.
-//  - workgroups of the matrix-core kernel have 4 waves (GQA_WAVES = 8 or 16
-//    overrides where the register budget for the head blocks allows).
+//    calls take the VALU kernel, whose one-round plan splits less); binary32
+//    uses its own matrix-core kernel for r = 3..64 (one workgroup per block
+//    of 16 heads) and the VALU kernel for r <= 2.  GQA_KERNEL=valu|mfma
+//    overrides.
+//  - workgroups of the matrix-core kernels have 4 waves (GQA_WAVES = 8 or 16
+//    overrides for bfloat16 where the register budget for the head blocks
+//    allows).
 //  - with fewer (b, g) units than compute units the matrix-core kernel
 //    spreads a group's head blocks over up to 2 or 4 workgroups (head chunks;
 //    how many by an estimate of the busiest compute unit's work, see
@@ -148,21 +151,21 @@ gqa_status check_shape(int B, int H, int G, int d, int Lmax, gqa_dtype dt) {
 //    plain instead of non-temporal loads (GQA_TEMPORAL=0/1 overrides) so
 //    that they share its lines in L2.
 //  - splits: one workgroup per (b, g, head chunk, split), split lengths of
-//    at least 256 positions (matrix cores) or 32 (VALU), at least Lmax/256,
+//    at least 256 positions (bfloat16 matrix cores), 64 (binary32 matrix
+//    cores) or 32 (VALU), at least Lmax/256,
 //    at most GQA_MAX_CHUNK = 8192 on the matrix cores, 4096 on the VALU
 //    kernel (the cap keeps ragged batches balanced).
 //    The VALU kernel aims at one workgroup per compute unit (three on
-//    binary32 with 4 or more heads per row set); the matrix-core kernel takes
+//    binary32 with 4 or more heads per row set); the matrix-core kernels take
 //    the split count of lowest plan_cost among those filling 1..4 rounds of
-//    256 workgroups.  GQA_TARGET_WGS (a plain workgroup target) and
-//    GQA_CHUNK override.
+//    256 workgroups (binary32 grids of one round: their own estimate).
+//    GQA_TARGET_WGS (a plain workgroup target) and GQA_CHUNK override.
 //  - when a sequence spans several splits, the workgroup that finishes its
 //    (b, g) unit last merges the partials inside the same kernel; with more
 //    units than counters (or GQA_MERGE=kernel) a second kernel merges instead.
-//    Beyond GQA_FUSED_MAX_SPLITS = 32 splits the wide merge kernel does (a
-//    launch of its own costs more than the in-kernel merge saves below that:
-//    at most 4% faster at 16-32 splits with 16 heads per group, up to 40%
-//    slower elsewhere).
+//    Beyond GQA_FUSED_MAX_SPLITS = 32 splits, or when that workgroup would
+//    read more than 96 KiB of partials, the wide merge kernel does (a launch
+//    of its own costs more than the in-kernel merge saves below that).
 //  - grids of more than 1024 workgroups with at least 4 splits per sequence
 //    (several dispatch rounds) take their items largest first, in an order a
 //    small kernel sorts from the lengths on the device (GQA_ORDER=0/1).
