@@ -519,6 +519,25 @@ def test_non_default_stream(env):
     check(out, oracle_out(q, k, v, lens, scale), "bf16", "side stream")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("plan", ["fused", "merge_kernel", "wide", "ordered"])
+def test_decode_in_two_phases(env, dtype, plan):
+    """gqa_decode_phase: phase 1 (the split kernel, with the order kernel
+    before it when the plan orders) then phase 2 (the separate merge kernel,
+    nothing when the merge runs in the split kernel) on one stream give
+    exactly what gqa_decode gives."""
+    env(GQA_CHUNK=64 if plan != "wide" else 32, GQA_MERGE="kernel" if plan == "merge_kernel" else None,
+        GQA_ORDER=1 if plan == "ordered" else None)
+    q, k, v, lt, scale = rand_case(5, 32, 8, 128, 1900, [1900, 1, 640, 1899, 33], dtype, seed=16)
+    ref = run_gpu(q, k, v, lt, scale).clone()
+    out = torch.full_like(ref, float("nan"))
+    gqa.decode_phase(1, q, k, v, lt, scale, out=out)
+    gqa.decode_phase(2, q, k, v, lt, scale, out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref), "%s %s" % (dtype, plan)
+    check(out, oracle_out(q, k, v, lt, scale), dtype, "two phases %s %s" % (dtype, plan))
+
+
 def test_concurrent_streams(env):
     """Two side streams (default priority) each running split plans at the
     same time, with no synchronisation between them: the binding keeps one
