@@ -325,6 +325,52 @@ def test_kernel_selection(lib, monkeypatch):
     assert lib.gqa_decode_kernel_kind(1, 64, 1, 64, 256, F32) == 1     # r = 64: four head chunks
 
 
+def test_plan_invariants_random_shapes(lib, monkeypatch):
+    """2000 seeded random shapes through the host plan, both dtypes: the
+    kernel follows the documented rule (bf16: matrix cores for r = 2..64 and
+    for MHA calls of at least 32 MiB; binary32: matrix cores for r = 3..64),
+    and the workspace is zero or exactly that of one split count S (at most
+    256 splits, or Lmax over the split cap where that is more), with an order
+    region of one int per workgroup for ordered grids."""
+    import numpy as np
+    for k in ("GQA_CHUNK", "GQA_TARGET_WGS", "GQA_MAX_CHUNK", "GQA_KERNEL", "GQA_HEAD_SPLIT", "GQA_MERGE", "GQA_ORDER",
+              "GQA_FUSED_MAX_SPLITS", "GQA_WAVES"):
+        monkeypatch.delenv(k, raising=False)
+    up = lambda x: (x + 255) // 256 * 256
+    rng = np.random.default_rng(99)
+    for _ in range(2000):
+        G = int(rng.choice([1, 2, 3, 4, 8, 16, 32]))
+        r = int(rng.choice([1, 2, 3, 4, 5, 8, 12, 16, 24, 32, 48, 64, 96, 128]))
+        B = int(rng.integers(1, 300))
+        d = int(rng.choice([64, 128]))
+        L = int(rng.choice([1, 7, 33, 256, 1000, 4096, 8192, 32768, 131072, 1 << 21]))
+        dt = int(rng.choice([F32, BF16]))
+        H = G * r
+        kind = lib.gqa_decode_kernel_kind(B, H, G, d, L, dt)
+        big_mha = 4.0 * B * G * L * d >= 32 * 1024 * 1024
+        want = (1 if (2 <= r <= 64 or (r == 1 and big_mha)) else 0) if dt == BF16 else (1 if 3 <= r <= 64 else 0)
+        assert kind == want, (B, H, G, d, L, dt)
+        ws = lib.gqa_decode_workspace_size(B, H, G, d, L, dt)
+        if ws == 0:
+            continue
+        cap = 8192 if kind == 1 else 4096
+        s_max = max(256, -(-L // cap))
+        est = (ws - 256 * 1024) // (B * H * (8 + 4 * d))
+        found = None
+        # the order region (one int per workgroup, <= 16 head chunks) adds at most a quarter to est
+        for S in range(max(2, est * 3 // 4 - 2), min(s_max, est + 2) + 1):
+            body = 256 * 1024 + up(B * H * S * 8) + B * H * S * d * 4
+            if ws == body:
+                found = S
+                break
+            extra = ws - (256 * 1024 + up(B * H * S * 8) + up(B * H * S * d * 4))
+            if extra > 0 and extra % (4 * B * G * S) == 0 and extra // (4 * B * G * S) <= 16:  # head chunks <= 16
+                found = S
+                break
+        assert found is not None, (B, H, G, d, L, dt, ws)
+        assert 2 <= found <= s_max, (B, H, G, d, L, dt, found)
+
+
 def test_meanpool_argument_errors(lib):
     mp = lib.gqa_meanpool_kv
     assert mp(P, 16, 6, 4, 8, P, None) == SHAPE
