@@ -485,23 +485,27 @@ SERVING_BL = [(1, 1024), (1, 32768), (1, 131072), (3, 8192), (4, 8192), (12, 409
 def shapes_bench(args):
     """One JSON line per serving shape: time per gqa_decode call (HIP events
     over back-to-back calls, inputs rotated through >= 1 GiB where memory
-    allows) and algorithmic bytes / time against 8 TB/s."""
+    allows) and algorithmic bytes / time against 8 TB/s (bf16, or the
+    dtype given)."""
     import torch
     import grouped_query_kv_decode_amd as gqa
     from grouped_query_kv_decode_amd import workloads as wl
     dev = torch.device("cuda:0")
     gqa.load_library()
     stream = torch.cuda.current_stream()
+    dtype = args.dtype or "bf16"
+    e = 4 if dtype == "f32" else 2
+    code = gqa.GQA_F32 if dtype == "f32" else gqa.GQA_BF16
     for (H, G, d) in SERVING_HEADS:
         for (B, L) in SERVING_BL:
-            kvb = 2 * B * G * L * d * 2
+            kvb = 2 * B * G * L * d * e
             if kvb > (8 << 30):
                 continue
-            w = wl.Workload("serving_B%d_H%d_G%d_d%d_L%d" % (B, H, G, d, L), B, H, G, d, L, "bf16", 5)
+            w = wl.Workload("serving_B%d_H%d_G%d_d%d_L%d" % (B, H, G, d, L), B, H, G, d, L, dtype, 5)
             rot = min(16, max(2, (1 << 30) // kvb))
             sets = [wl.make_inputs(w, dev, pad="none", seed_offset=i) for i in range(rot)]
             decs = [gqa.Decoder(q, k, v, lens, w.scale) for (q, k, v, lens) in sets]
-            ab = kvb + 2 * B * H * d * 2
+            ab = kvb + 2 * B * H * d * e
             for i in range(10):
                 decs[i % rot]()
             n = max(20, min(400, int(2e5 / max(1.0, ab / 7e6))))
@@ -513,9 +517,9 @@ def shapes_bench(args):
             e1.record(stream)
             torch.cuda.synchronize()
             us = e0.elapsed_time(e1) * 1e3 / n
-            kind = gqa.decode_kernel_kind(B, H, G, d, L, gqa.GQA_BF16)
-            splits = gqa.decode_workspace_size(B, H, G, d, L, gqa.GQA_BF16) > 0
-            print(json.dumps({"mode": "shapes", "B": B, "H": H, "G": G, "d": d, "Lmax": L, "dtype": "bf16",
+            kind = gqa.decode_kernel_kind(B, H, G, d, L, code)
+            splits = gqa.decode_workspace_size(B, H, G, d, L, code) > 0
+            print(json.dumps({"mode": "shapes", "B": B, "H": H, "G": G, "d": d, "Lmax": L, "dtype": dtype,
                               "kernel": ["valu", "mfma"][kind], "split": splits, "steps": n, "rotation_sets": rot,
                               "us_per_call": us, "alg_bytes": ab, "alg_GBps": ab / us / 1e3,
                               "frac_of_8TBps": ab / us / 8e6}), flush=True)

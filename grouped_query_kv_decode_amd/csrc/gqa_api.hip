@@ -139,8 +139,9 @@ gqa_status check_shape(int B, int H, int G, int d, int Lmax, gqa_dtype dt) {
 //    for r = 1 on calls that stream at least 32 MiB of K and V (smaller MHA
 //    calls take the VALU kernel, whose one-round plan splits less); binary32
 //    uses its own matrix-core kernel for r = 3..64 (one workgroup per block
-//    of 16 heads) and the VALU kernel for r <= 2.  GQA_KERNEL=valu|mfma
-//    overrides.
+//    of 16 heads), and for r <= 2 on calls of at least 32 MiB whose (b, g)
+//    units do not fill whole rounds of 256 workgroups; otherwise the VALU
+//    kernel.  GQA_KERNEL=valu|mfma overrides.
 //  - workgroups of the matrix-core kernels have 4 waves (GQA_WAVES = 8 or 16
 //    overrides for bfloat16 where the register budget for the head blocks
 //    allows).
@@ -187,14 +188,25 @@ gqa_status make_plan(int B, int H, int G, int d, int Lmax, gqa_dtype dt, const T
   // B32 H64 G4 d64 L2048 25.0 / 62.7, B8 H48 G4 d128 L4096 27.2 / 64.5,
   // B1 H8 G2 d64 L256 6.8 / 8.8; r = 24..64: B16 H48 G2 d128 L4096 33.3 /
   // 88.8, B8 H64 G2 d128 L4096 21.7 / 66.9, B32 H64 G1 d64 L2048 18.9 / 66.8,
-  // B4 H64 G1 d128 L8192 23.7 / 75.9.  At r = 2 and r = 1 the two are within
-  // 1% (B8 H32 G16 d128 L8192 156.9 / 156.0, B16 H16 G8 d128 L4096 82.0 /
-  // 81.8, B8 H32 G32 d128 L4096 154.8 / 153.5) and the VALU kernel stays.
+  // B4 H64 G1 d128 L8192 23.7 / 75.9.  At r = 2 and r = 1 the kernels
+  // themselves tie (B8 H32 G16 d128 L8192 156.9 / 156.0, B16 H16 G8 d128
+  // L4096 82.0 / 81.8, B8 H32 G32 d128 L4096 154.8 / 153.5, B16 H32 G32 d128
+  // L1024 82.4 / 79.1), and the VALU kernel stays - except on calls of at
+  // least 32 MiB whose (b, g) units do not fill whole rounds of 256
+  // workgroups (neither divides the other), where the matrix-core plan's
+  // split count, chosen to fill whole rounds, wins (graph replays): r = 2
+  // B20 H32 G16 d128 L4096 (320 units) 202.4 / 230.7 us, B6 H32 G16 d128
+  // L8192 123.1 / 154.2, B3 H32 G16 d128 L8192 65.4 / 80.4, B12 H32 G16 d128
+  // L4096 121.8 / 126.3, B40 H32 G16 d128 L2048 196.8 / 199.9; r = 1 B3 H32
+  // G32 d128 L8192 121.5 / 151.8, B20 H16 G16 d128 L4096 201.2 / 226.0, B6
+  // H32 G32 d128 L4096 120.6 / 123.3.
   const double kv_bytes = 4.0 * B * G * (double)Lmax * d;
   const bool mha_on_mfma = r == 1 && kv_bytes >= 32.0 * 1024 * 1024;
-  int kind = (dt == GQA_BF16 && ((r >= 2 && r <= 64) || mha_on_mfma)) || (dt == GQA_F32 && r >= 3 && r <= 64)
-                 ? KIND_MFMA
-                 : KIND_VALU;
+  const long bg = (long)B * G;
+  const bool uneven_rounds = bg % 256 != 0 && 256 % bg != 0;
+  const bool f32_mfma = dt == GQA_F32 && ((r >= 3 && r <= 64) ||
+                                          (r <= 2 && uneven_rounds && 2.0 * kv_bytes >= 32.0 * 1024 * 1024));
+  int kind = (dt == GQA_BF16 && ((r >= 2 && r <= 64) || mha_on_mfma)) || f32_mfma ? KIND_MFMA : KIND_VALU;
   if (tu.kernel == 1 + KIND_VALU) kind = KIND_VALU;
   if (tu.kernel == 1 + KIND_MFMA && r <= 64) kind = KIND_MFMA;
   pl->kind = kind;

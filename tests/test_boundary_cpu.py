@@ -308,6 +308,10 @@ def test_kernel_selection(lib, monkeypatch):
     assert lib.gqa_decode_kernel_kind(1, 8, 2, 64, 256, F32) == 1     # binary32, r = 4: matrix cores
     assert lib.gqa_decode_kernel_kind(8, 48, 4, 128, 4096, F32) == 1  # r = 12
     assert lib.gqa_decode_kernel_kind(8, 32, 16, 128, 8192, F32) == 0  # r = 2: the VALU kernel
+    assert lib.gqa_decode_kernel_kind(20, 32, 16, 128, 4096, F32) == 1  # r = 2, 320 units: matrix cores
+    assert lib.gqa_decode_kernel_kind(6, 32, 32, 128, 4096, F32) == 1   # r = 1, 192 units: matrix cores
+    assert lib.gqa_decode_kernel_kind(16, 32, 32, 128, 1024, F32) == 0  # r = 1, 512 units: VALU
+    assert lib.gqa_decode_kernel_kind(3, 8, 8, 64, 256, F32) == 0       # r = 1, 24 units but 3 MiB: VALU
     assert lib.gqa_decode_kernel_kind(8, 32, 32, 128, 4096, F32) == 0  # r = 1
     assert lib.gqa_decode_kernel_kind(1, 32, 1, 64, 256, F32) == 1     # r = 32: two head blocks
     assert lib.gqa_decode_kernel_kind(1, 128, 1, 64, 256, F32) == 0    # r = 128
@@ -328,7 +332,9 @@ def test_kernel_selection(lib, monkeypatch):
 def test_plan_invariants_random_shapes(lib, monkeypatch):
     """2000 seeded random shapes through the host plan, both dtypes: the
     kernel follows the documented rule (bf16: matrix cores for r = 2..64 and
-    for MHA calls of at least 32 MiB; binary32: matrix cores for r = 3..64),
+    for MHA calls of at least 32 MiB; binary32: matrix cores for r = 3..64,
+    and for r <= 2 on calls of at least 32 MiB whose B*G units neither divide
+    nor are a multiple of 256),
     and the workspace is zero or exactly that of one split count S (at most
     256 splits, or Lmax over the split cap where that is more), with an order
     region of one int per workgroup for ordered grids."""
@@ -348,7 +354,9 @@ def test_plan_invariants_random_shapes(lib, monkeypatch):
         H = G * r
         kind = lib.gqa_decode_kernel_kind(B, H, G, d, L, dt)
         big_mha = 4.0 * B * G * L * d >= 32 * 1024 * 1024
-        want = (1 if (2 <= r <= 64 or (r == 1 and big_mha)) else 0) if dt == BF16 else (1 if 3 <= r <= 64 else 0)
+        uneven = (B * G) % 256 != 0 and 256 % (B * G) != 0
+        f32_mfma = 3 <= r <= 64 or (r <= 2 and uneven and 8.0 * B * G * L * d >= 32 * 1024 * 1024)
+        want = (1 if (2 <= r <= 64 or (r == 1 and big_mha)) else 0) if dt == BF16 else (1 if f32_mfma else 0)
         assert kind == want, (B, H, G, d, L, dt)
         ws = lib.gqa_decode_workspace_size(B, H, G, d, L, dt)
         if ws == 0:
