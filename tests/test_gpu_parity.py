@@ -333,6 +333,8 @@ PLAN_SHAPES = [
     (1, 8, 2, 64, 1024, "f32"),        # binary32 matrix cores, one-round grid: 16 splits of 64 by the estimate
     (2, 64, 1, 64, 4096, "f32"),       # binary32 matrix cores, r = 64: four head chunks
     (8, 32, 16, 128, 4096, "f32"),     # binary32 r = 2: the VALU kernel
+    (20, 32, 16, 128, 4096, "f32"),    # binary32 r = 2, 320 units (not whole rounds): matrix cores
+    (3, 32, 32, 128, 8192, "f32"),     # binary32 r = 1, 96 units: matrix cores
     (4, 32, 32, 64, 512, "bf16"),      # VALU (r = 1): 2 -> 1 split by the estimate
     (64, 64, 8, 128, 16384, "bf16"),   # 8192-position split cap: 2 splits, 1024 workgroups
 ]
