@@ -838,6 +838,26 @@ def test_ragged_workload_binary32(env):
           at_output_scale=True)
 
 
+@pytest.mark.parametrize("dtype,B,H", [("bf16", 256, 64), ("f32", 128, 32)])
+def test_largest_caches(env, dtype, B, H):
+    """Caches past 2^32 elements per tensor (G8 d128 Lmax 32768: 8.6e9 bf16
+    or 4.3e9 binary32 elements, 17 GB each): every address computed past
+    32 bits.  Ragged lengths (4 splits, an ordered grid of several rounds);
+    sequences sampled against the oracle, every output finite."""
+    G, d, L = 8, 128, 32768
+    gen = torch.Generator().manual_seed(4242 + B)
+    lens = [int(x) for x in torch.randint(1, L + 1, (B,), generator=gen)]
+    lens[0], lens[-1] = L, L
+    w = wl.Workload("largest", B, H, G, d, L, dtype, 77)
+    q, k, v, lt = wl.make_inputs(w, DEV, pad="none", seq_lens=torch.tensor(lens, dtype=torch.int32))
+    out = run_gpu(q, k, v, lt, w.scale)
+    assert torch.isfinite(out).all()
+    rows = [0, 1, B // 2, B - 1]
+    check(out.cpu()[rows], oracle_out(q, k, v, lt, w.scale, rows=rows), dtype, "largest caches %s B%d" % (dtype, B))
+    del q, k, v, out
+    torch.cuda.empty_cache()
+
+
 def test_ragged_workload(env):
     """Ragged long-context workload at full size (B64 H64 G8 d128, lengths
     uniform in 1..32768 over a 32768-position padded cache): every one of the
