@@ -838,17 +838,22 @@ def test_ragged_workload_binary32(env):
           at_output_scale=True)
 
 
-@pytest.mark.parametrize("dtype,B,H", [("bf16", 256, 64), ("f32", 128, 32)])
-def test_largest_caches(env, dtype, B, H):
-    """Caches past 2^32 elements per tensor (G8 d128 Lmax 32768: 8.6e9 bf16
-    or 4.3e9 binary32 elements, 17 GB each): every address computed past
-    32 bits.  Ragged lengths (4 splits, an ordered grid of several rounds);
-    sequences sampled against the oracle, every output finite."""
-    G, d, L = 8, 128, 32768
+@pytest.mark.parametrize("dtype,B,H,G", [("bf16", 256, 64, 8), ("f32", 128, 32, 8), ("f32", 64, 32, 16)],
+                         ids=["bf16_mfma", "f32_mfma", "f32_valu"])
+def test_largest_caches(env, dtype, B, H, G):
+    """Caches past 2^32 elements per tensor (d128 Lmax 32768: 8.6e9 bf16 or
+    4.3e9 binary32 elements, 17 GB each), on both matrix-core kernels and
+    the VALU kernel (binary32, two heads per K/V head): every address
+    computed past 32 bits.  Ragged lengths (several splits, an ordered grid
+    of several rounds); sequences sampled against the oracle, every output
+    finite."""
+    d, L = 128, 32768
     gen = torch.Generator().manual_seed(4242 + B)
     lens = [int(x) for x in torch.randint(1, L + 1, (B,), generator=gen)]
     lens[0], lens[-1] = L, L
     w = wl.Workload("largest", B, H, G, d, L, dtype, 77)
+    want_kind = 0 if G == 16 else 1
+    assert gqa.decode_kernel_kind(B, H, G, d, L, gqa.GQA_F32 if dtype == "f32" else gqa.GQA_BF16) == want_kind
     q, k, v, lt = wl.make_inputs(w, DEV, pad="none", seq_lens=torch.tensor(lens, dtype=torch.int32))
     out = run_gpu(q, k, v, lt, w.scale)
     assert torch.isfinite(out).all()
